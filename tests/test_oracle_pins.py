@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: each test checks it against a
+value the pages print, a closed form, brute force, a special case that
+reduces to a plain product written out with loops, or the independent
+capacity implementation in capacity_fixed_point.py.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from capacity_fixed_point import capacity_route_fixed_point
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ---------------------------------------------------------------- helpers written out with loops
+def naive_matmul_t(a, w):
+    """a [M, K] times w^T, w stored [Nout, K]; pure Python loops in float64."""
+    M, K = len(a), len(a[0])
+    return [[sum(float(a[m][i]) * float(w[n][i]) for i in range(K)) for n in range(len(w))] for m in range(M)]
+
+
+def naive_ffn(x, w_up, w_down, ffn, w_gate=None):
+    if ffn == O.RELU2:
+        h = [[max(v, 0.0) for v in row] for row in naive_matmul_t(x, w_up)]
+    else:
+        g = naive_matmul_t(x, w_gate)
+        u = naive_matmul_t(x, w_up)
+        h = [[gv / (1.0 + math.exp(-gv)) * uv for gv, uv in zip(gr, ur)] for gr, ur in zip(g, u)]
+    return np.array(naive_matmul_t(h, w_down))
+
+
+def naive_softmax(v):
+    m = max(v)
+    e = [math.exp(a - m) for a in v]
+    s = sum(e)
+    return [a / s for a in e]
+
+
+def rand_layer(rng, T, d, N, d_ff, ffn):
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((N, d)) / math.sqrt(d)
+    wg = rng.standard_normal((N, d_ff, d)) / math.sqrt(d) if ffn == O.SWIGLU else None
+    wu = rng.standard_normal((N, d_ff, d)) / math.sqrt(d)
+    wd = rng.standard_normal((N, d, d_ff)) / math.sqrt(d_ff)
+    return x, wr, wg, wu, wd
+
+
+# ---------------------------------------------------------------- counting (printed values)
+def test_toy_param_count_matches_page():
+    (row,) = _golden_rows("toy_param_count.txt")
+    kv = dict(item.split("=") for item in row)
+    total, active = O.param_counts(int(kv["N"]), int(kv["d"]), int(kv["k"]), O.LINEAR)
+    assert total == int(kv["total"]) and active == int(kv["active"])
+    assert f"{active / total:.2f}" == kv["ratio"]
+
+
+def test_active_expert_fraction_matches_pages():
+    for N, k, pct, dec in _golden_rows("active_fraction.txt"):
+        N, k, dec = int(N), int(k), int(dec)
+        total, active = O.param_counts(N, 64, k, O.SWIGLU, d_ff=32)
+        router = 64 * N
+        frac = 100.0 * (active - router) / (total - router)
+        assert f"{frac:.{dec}f}" == pct, (N, k, frac, pct)
+
+
+def test_param_counts_shared_expert_counts_as_always_active():
+    t0, a0 = O.param_counts(256, 7168, 8, O.SWIGLU, d_ff=2048)
+    t1, a1 = O.param_counts(256, 7168, 8, O.SWIGLU, d_ff=2048, n_shared=1)
+    per = 3 * 7168 * 2048
+    assert t1 - t0 == per and a1 - a0 == per
+
+
+# ---------------------------------------------------------------- worked combine (page 1, step 6)
+@pytest.mark.parametrize("gating", [O.TOPK_SOFTMAX, O.SOFTMAX_TOPK])
+def test_worked_combine_two_experts(gating):
+    # Experts 2 and 5 get scores 0.6 and 0.4; the output is 0.6 E2(x) + 0.4 E5(x).
+    # Expert e is relu(x I) (c_e I): on x > 0 it returns c_e * x exactly.
+    N, d = 8, 4
+    z = np.full((1, N), -200.0)
+    z[0, 2] = math.log(0.6)
+    z[0, 5] = math.log(0.4)
+    c = np.arange(1, N + 1, dtype=np.float64)
+    w_up = np.stack([np.eye(d)] * N)
+    w_down = np.stack([c[e] * np.eye(d) for e in range(N)])
+    x = np.array([[0.5, 1.0, 2.0, 3.0]])
+    out = O.forward(x, None, w_up, w_down, 2, O.RELU2, gating, z=z)
+    assert out["idx"].tolist() == [[2, 5]]
+    assert np.allclose(out["w"], [[0.6, 0.4]], atol=1e-12, rtol=0)
+    assert np.allclose(out["y"], (0.6 * c[2] + 0.4 * c[5]) * x, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------- top-k
+def test_topk_set_is_brute_force_best_subset_with_ties():
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        N = int(rng.integers(1, 7))
+        z = rng.integers(-2, 3, size=(30, N)).astype(np.float64)   # many exact ties
+        for k in range(1, N + 1):
+            idx, _ = O.topk_route(z, k, O.TOPK_SOFTMAX)
+            for t in range(z.shape[0]):
+                best = max(itertools.combinations(range(N), k),
+                           key=lambda s: (sum(z[t, list(s)]), [-e for e in s]))
+                assert sorted(idx[t].tolist()) == list(best)
+                zs = z[t, idx[t]]
+                for j in range(k - 1):            # slot order: descending, ties to lower id
+                    assert zs[j] > zs[j + 1] or (zs[j] == zs[j + 1] and idx[t, j] < idx[t, j + 1])
+
+
+def test_both_gating_modes_pick_the_same_experts():
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((64, 16))
+    ia, _ = O.topk_route(z, 4, O.TOPK_SOFTMAX)
+    ib, _ = O.topk_route(z, 4, O.SOFTMAX_TOPK)
+    assert np.array_equal(ia, ib)
+
+
+def test_gate_weight_invariants_and_closed_forms():
+    rng = np.random.default_rng(7)
+    z = 3.0 * rng.standard_normal((50, 12))
+    for k in (1, 2, 5, 12):
+        ia, wa = O.topk_route(z, k, O.TOPK_SOFTMAX)
+        ib, wb = O.topk_route(z, k, O.SOFTMAX_TOPK)
+        assert np.allclose(wa.sum(axis=1), 1.0, atol=1e-12)
+        assert (np.diff(wa, axis=1) <= 1e-15).all()           # best slot has the largest weight
+        for t in range(z.shape[0]):
+            p = naive_softmax(z[t].tolist())
+            assert np.allclose(wb[t], [p[e] for e in ib[t]], atol=1e-14, rtol=0)
+            assert np.allclose(wa[t], naive_softmax([z[t, e] for e in ia[t]]), atol=1e-14, rtol=0)
+        assert (wb.sum(axis=1) <= 1.0 + 1e-12).all()
+        if k == 12:
+            assert np.allclose(wb.sum(axis=1), 1.0, atol=1e-12)
+            assert np.allclose(wa, wb, atol=1e-14)               # k = N: the two modes coincide
+    # k = 1 in mode A always gives weight exactly 1
+    _, w1 = O.topk_route(z, 1, O.TOPK_SOFTMAX)
+    assert (w1 == 1.0).all()
+
+
+def test_softmax_is_shift_invariant_and_stable_for_large_logits():
+    z = np.array([[1000.0, 999.0, -1000.0]])
+    _, w = O.topk_route(z, 2, O.TOPK_SOFTMAX)
+    e = math.exp(-1.0)
+    assert np.allclose(w, [[1 / (1 + e), e / (1 + e)]], atol=1e-15, rtol=0)
+
+
+# ---------------------------------------------------------------- FFN
+def test_silu_closed_form_points():
+    u = np.array([0.0, 1.0, -1.0, 2.0, -30.0, 40.0])
+    want = [0.0, 0.7310585786300049, -0.2689414213699951, 1.7615941559557649,
+            -30.0 * 9.357622968840175e-14, 40.0]
+    assert np.allclose(O.silu(u), want, rtol=1e-12, atol=1e-20)
+
+
+@pytest.mark.parametrize("ffn", [O.RELU2, O.SWIGLU])
+def test_expert_ffn_against_written_out_products(ffn):
+    rng = np.random.default_rng(8)
+    M, d, d_ff = 3, 5, 7                      # non-square: a transposed operand cannot pass
+    x = rng.standard_normal((M, d))
+    wg = rng.standard_normal((d_ff, d))
+    wu = rng.standard_normal((d_ff, d))
+    wd = rng.standard_normal((d, d_ff))
+    got = O.expert_ffn(x, wu, wd, ffn, wg if ffn == O.SWIGLU else None)
+    want = naive_ffn(x.tolist(), wu.tolist(), wd.tolist(), ffn, wg.tolist())
+    assert got.shape == (M, d)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_router_logits_against_written_out_product_and_bias():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((4, 6))
+    wr = rng.standard_normal((3, 6))
+    b = np.array([0.5, -1.0, 2.0])
+    want = np.array(naive_matmul_t(x.tolist(), wr.tolist())) + b
+    assert np.allclose(O.router_logits(x, wr, b), want, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- whole-layer special cases
+@pytest.mark.parametrize("ffn", [O.RELU2, O.SWIGLU])
+def test_k_equals_n_is_dense_softmax_mixture(ffn):
+    rng = np.random.default_rng(10)
+    T, d, N, d_ff = 6, 4, 5, 3
+    x, wr, wg, wu, wd = rand_layer(rng, T, d, N, d_ff, ffn)
+    z = O.router_logits(x, wr)
+    expert_out = [naive_ffn(x.tolist(), wu[e].tolist(), wd[e].tolist(), ffn,
+                            None if wg is None else wg[e].tolist()) for e in range(N)]
+    want = np.zeros((T, d))
+    for t in range(T):
+        p = naive_softmax(z[t].tolist())
+        for e in range(N):
+            want[t] += p[e] * expert_out[e][t]
+    for gating in (O.TOPK_SOFTMAX, O.SOFTMAX_TOPK):
+        out = O.forward(x, wr, wu, wd, N, ffn, gating, w_gate=wg)
+        assert np.allclose(out["y"], want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("ffn", [O.RELU2, O.SWIGLU])
+def test_identical_experts_reduce_to_one_ffn(ffn):
+    rng = np.random.default_rng(11)
+    T, d, N, d_ff, k = 7, 4, 6, 5, 3
+    x, wr, wg, wu, wd = rand_layer(rng, T, d, N, d_ff, ffn)
+    wu[:] = wu[0]
+    wd[:] = wd[0]
+    if wg is not None:
+        wg[:] = wg[0]
+    want = naive_ffn(x.tolist(), wu[0].tolist(), wd[0].tolist(), ffn, None if wg is None else wg[0].tolist())
+    out = O.forward(x, wr, wu, wd, k, ffn, O.TOPK_SOFTMAX, w_gate=wg)
+    assert np.allclose(out["y"], want, rtol=1e-12, atol=1e-12)
+    outb = O.forward(x, wr, wu, wd, k, ffn, O.SOFTMAX_TOPK, w_gate=wg)
+    assert np.allclose(outb["y"], outb["w"].sum(axis=1, keepdims=True) * want, rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_plain_ffn():
+    rng = np.random.default_rng(12)
+    x, wr, wg, wu, wd = rand_layer(rng, 5, 4, 1, 6, O.SWIGLU)
+    out = O.forward(x, wr, wu, wd, 1, O.SWIGLU, O.TOPK_SOFTMAX, w_gate=wg)
+    want = naive_ffn(x.tolist(), wu[0].tolist(), wd[0].tolist(), O.SWIGLU, wg[0].tolist())
+    assert np.allclose(out["y"], want, rtol=1e-12, atol=1e-12)
+    assert out["counts"].tolist() == [5]
+
+
+def test_page_toy_layer_semantics():
+    # The toy of page 2 (section 代码): experts are single d x d linears, top-k by
+    # argsort, softmax over the picked logits, weighted sum of x @ W_e.  A ReLU
+    # expert with W1 = I sees x > 0 unchanged, so it is the toy's linear expert.
+    rng = np.random.default_rng(13)
+    N, d, k, T = 8, 16, 2, 10
+    experts_W = rng.standard_normal((N, d, d)) / d
+    router_W = rng.standard_normal((d, N))
+    x = np.abs(rng.standard_normal((T, d))) + 0.01
+    want = np.zeros((T, d))
+    for t in range(T):
+        gate = [sum(x[t, i] * router_W[i, e] for i in range(d)) for e in range(N)]
+        top = sorted(range(N), key=lambda e: gate[e])[-k:]
+        w = naive_softmax([gate[e] for e in top])
+        for wi, e in zip(w, top):
+            want[t] += wi * np.array(naive_matmul_t([x[t].tolist()], experts_W[e].T.tolist())[0])
+    out = O.forward(x, router_W.T, np.stack([np.eye(d)] * N), np.transpose(experts_W, (0, 2, 1)),
+                    k, O.RELU2, O.TOPK_SOFTMAX)
+    assert np.allclose(out["y"], want, rtol=1e-11, atol=1e-12)
+
+
+def test_shared_expert_adds_plain_ffn_with_weight_one():
+    rng = np.random.default_rng(14)
+    T, d, N, d_ff, k = 6, 4, 5, 3, 2
+    x, wr, wg, wu, wd = rand_layer(rng, T, d, N, d_ff, O.SWIGLU)
+    sg, su, sd = rng.standard_normal((d_ff, d)), rng.standard_normal((d_ff, d)), rng.standard_normal((d, d_ff))
+    base = O.forward(x, wr, wu, wd, k, O.SWIGLU, O.SOFTMAX_TOPK, w_gate=wg)
+    with_sh = O.forward(x, wr, wu, wd, k, O.SWIGLU, O.SOFTMAX_TOPK, w_gate=wg, shared=(sg, su, sd))
+    want_sh = naive_ffn(x.tolist(), su.tolist(), sd.tolist(), O.SWIGLU, sg.tolist())
+    assert np.allclose(with_sh["y"] - base["y"], want_sh, rtol=1e-11, atol=1e-12)
+    assert with_sh["counts"].sum() == T * k
+
+
+def test_token_subset_matches_full_evaluation():
+    rng = np.random.default_rng(15)
+    x, wr, wg, wu, wd = rand_layer(rng, 20, 8, 6, 5, O.SWIGLU)
+    full = O.forward(x, wr, wu, wd, 2, O.SWIGLU, O.TOPK_SOFTMAX, w_gate=wg, capacity_factor=1.0)
+    sub = O.forward(x, wr, wu, wd, 2, O.SWIGLU, O.TOPK_SOFTMAX, w_gate=wg, capacity_factor=1.0,
+                    tokens=[19, 3, 7])
+    assert np.allclose(sub["y"], full["y"][[19, 3, 7]], rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------- grouping by expert
+def test_group_by_expert_invariants_and_brute_force():
+    rng = np.random.default_rng(16)
+    for trial in range(20):
+        T, k, N = int(rng.integers(1, 40)), int(rng.integers(1, 4)), int(rng.integers(1, 9))
+        idx = rng.integers(-1 if trial % 3 == 0 else 0, N, size=(T, k))
+        counts, offsets, perm, inv = O.group_by_expert(idx, N)
+        flat = idx.reshape(-1)
+        kept = [s for s in range(T * k) if flat[s] >= 0]
+        assert perm.tolist() == sorted(kept, key=lambda s: (flat[s], s))
+        assert counts.tolist() == [int((flat == e).sum()) for e in range(N)]
+        assert offsets[0] == 0 and offsets[-1] == len(kept)
+        assert np.array_equal(np.diff(offsets), counts)
+        for r, s in enumerate(perm):
+            assert inv[s] == r
+        assert all(inv[s] == -1 for s in range(T * k) if flat[s] < 0)
+
+
+# ---------------------------------------------------------------- capacity
+def test_capacity_value_of_the_skewed_layer():
+    assert O.expert_capacity(2.0, 16384, 2, 128) == 512
+    assert O.expert_capacity(2.0, 100, 2, 8) == 50
+    assert O.expert_capacity(1.0, 10, 1, 3) == 4           # ceil(10/3)
+
+
+def test_capacity_64_reading():
+    # capacity 64: a token whose first choice already holds 63 slots still fits
+    # (it becomes the 64th); the next one is re-routed to its next-best expert.
+    T, N = 66, 4
+    z = np.tile(np.array([3.0, 2.0, 1.0, 0.0]), (T, 1))
+    idx, w, fill = O.capacity_route(z, 1, 64)
+    assert idx[:64, 0].tolist() == [0] * 64
+    assert idx[64:, 0].tolist() == [1, 1]
+    assert fill.tolist() == [64, 2, 0, 0]
+    assert (w == 1.0).all()
+
+
+def test_capacity_drop_when_no_room_anywhere():
+    z = np.array([[1.0, 0.0], [1.0, 0.0]])
+    idx, w, fill = O.capacity_route(z, 2, 1)
+    assert idx.tolist() == [[0, -1], [1, -1]]
+    assert w.tolist() == [[1.0, 0.0], [1.0, 0.0]]
+    assert fill.tolist() == [1, 1]
+
+
+def _replay_ok(z, idx, C):
+    """Every slot's expert is the best one it could take at its turn."""
+    T, N = z.shape
+    k = idx.shape[1]
+    fill = [0] * N
+    for j in range(k):
+        for t in range(T):
+            e = idx[t, j]
+            held = set(idx[t, :j].tolist())
+            better = [f for f in range(N) if (z[t, f] > (z[t, e] if e >= 0 else -np.inf)) or
+                      (e >= 0 and z[t, f] == z[t, e] and f < e)]
+            if any(f not in held and fill[f] < C for f in better):
+                return False
+            if e < 0:
+                if any(f not in held and fill[f] < C for f in range(N)):
+                    return False
+            else:
+                if e in held or fill[e] >= C:
+                    return False
+                fill[e] += 1
+    return True
+
+
+def test_capacity_serial_equals_independent_fixed_point():
+    rng = np.random.default_rng(17)
+    for trial in range(60):
+        T = int(rng.integers(1, 60))
+        N = int(rng.integers(2, 9))
+        k = int(rng.integers(1, min(3, N) + 1))
+        C = int(rng.integers(1, max(2, T * k // N + 2)))
+        z = rng.standard_normal((T, N)) - 2.0 * np.log(np.arange(N) + 1.0)[None, :]
+        if trial % 4 == 0:
+            z = np.round(z)                       # exact ties
+        idx, w, fill = O.capacity_route(z, k, C)
+        idx2, fill2 = capacity_route_fixed_point(z, k, C)
+        assert np.array_equal(idx, idx2), (trial, T, N, k, C)
+        assert np.array_equal(fill, fill2)
+        assert (fill <= C).all()
+        for t in range(T):
+            kept = [e for e in idx[t] if e >= 0]
+            assert len(kept) == len(set(kept))
+        assert _replay_ok(z, idx, C)
+        if fill.sum() == T * k:
+            assert np.allclose(w.sum(axis=1), 1.0, atol=1e-12)
+
+
+def test_capacity_large_enough_equals_plain_topk():
+    rng = np.random.default_rng(18)
+    z = rng.standard_normal((40, 6))
+    for k in (1, 2, 3):
+        C = O.expert_capacity(6 / k, 40, k, 6)          # cf = N/k -> C = T: never binds
+        idx, w, _ = O.capacity_route(z, k, C)
+        idx0, w0 = O.topk_route(z, k, O.TOPK_SOFTMAX)
+        assert np.array_equal(idx, idx0)
+        assert np.allclose(w, w0, atol=0, rtol=0)
+
+
+def test_near_tie_detection():
+    z = np.array([[1.0, 1.0 + 5e-7, 0.0], [3.0, 2.0, 1.0], [0.0, 0.5, 0.5 + 2e-6]])
+    assert O.near_tie_tokens(z, depth=1).tolist() == [0]
+    assert O.near_tie_tokens(z, depth=2, threshold=3e-6).tolist() == [0, 2]

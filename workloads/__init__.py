@@ -1,0 +1,165 @@
+"""Seeded synthetic workloads for the sparse MoE layer forward.
+
+This module is shared harness: it only draws inputs (tokens, router weights,
+expert weights, the per-expert logit bias) and holds none of the layer's
+arithmetic.  Both the CPU oracle's tests and the GPU path's tests, smoke run
+and benchmark take their inputs from here, so the two sides see bit-identical
+values.
+
+Shapes come from the five layer configurations that the MoE pages describe in
+prose (Mixtral-8x7B: 8 experts, top-2; DeepSeek-V3: 256 routed + 1 shared
+expert, top-8; a 128-expert top-2 layer with an expert capacity of
+capacity_factor 2.0).  The pages publish no dataset or trained weights for any
+of them, so every tensor is drawn from a seeded Gaussian:
+
+  x ~ N(0, 1);  router and input-side expert weights ~ N(0, 1/d);
+  output-side expert weights ~ N(0, 1/d_ff);  values rounded to bf16 (RNE) on
+  the bf16 layers and kept in fp32 on the fp32 layer.
+
+The skewed layer adds a fixed per-expert logit bias b[e] = -2 ln(e + 1)
+(a Zipf-like preference for low expert ids), computed in float64 and rounded
+to fp32 once, so both sides read the same fp32 values.
+
+Weight layout (the layout the C ABI takes, see include/moe.h): every weight is
+stored output-major, one row per output feature holding its input-side
+weights contiguously -- the layout of a linear layer's weight matrix:
+
+  w_router [N, d]          z[t, e]   = sum_i x[t, i] * w_router[e, i]
+  w_gate   [N, d_ff, d]    g[t, f]   = sum_i x[t, i] * w_gate[e, f, i]
+  w_up     [N, d_ff, d]    u[t, f]   = sum_i x[t, i] * w_up[e, f, i]
+  w_down   [N, d, d_ff]    y[t, o]   = sum_f h[t, f] * w_down[e, o, f]
+  shared expert: sh_gate, sh_up [d_ff, d], sh_down [d, d_ff]
+
+For the two-layer ReLU expert, w_up holds W1 and w_down holds W2; w_gate is
+unused.
+
+Random draws use torch's counter-based generator (Philox on the GPU, its CPU
+generator on the host), one generator per tensor and per expert, seeded from
+(config seed, tensor stream, expert).  Draws on the GPU and on the host give
+different values for the same seed; a test that compares the two sides draws
+once on the GPU and copies the values to the host.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import torch
+
+# tensor streams (one generator stream per tensor)
+STREAM_X, STREAM_ROUTER, STREAM_GATE, STREAM_UP, STREAM_DOWN = 1, 2, 3, 4, 5
+STREAM_SH_GATE, STREAM_SH_UP, STREAM_SH_DOWN = 6, 7, 8
+
+FFN_RELU2 = "relu2"
+FFN_SWIGLU = "swiglu"
+GATE_TOPK_SOFTMAX = "topk_softmax"     # top-k, then softmax over the k picked logits
+GATE_SOFTMAX_TOPK = "softmax_topk"     # softmax over all N logits, then top-k, no renormalisation
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    T: int                  # tokens (rows of x)
+    d: int                  # model width
+    N: int                  # routed experts
+    k: int                  # experts per token
+    d_ff: int               # expert hidden width
+    dtype: str              # "f32" or "bf16": weights and activations
+    ffn: str                # FFN_RELU2 or FFN_SWIGLU
+    gating: str             # GATE_TOPK_SOFTMAX or GATE_SOFTMAX_TOPK
+    capacity_factor: float = 0.0   # <= 0: unlimited
+    has_shared: bool = False       # one shared expert applied to every token, weight 1
+    zipf_bias: bool = False        # per-expert logit bias b[e] = -2 ln(e + 1)
+    seed: int = 0
+
+    def replace(self, **kw) -> "LayerConfig":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+CONFIGS: Dict[str, LayerConfig] = {
+    # tiny fp32 layer: 8 experts, top-2, two-layer ReLU experts d -> 256 -> d
+    "tiny_fp32": LayerConfig("tiny_fp32", T=128, d=64, N=8, k=2, d_ff=256, dtype="f32",
+                             ffn=FFN_RELU2, gating=GATE_TOPK_SOFTMAX, seed=1001),
+    # Mixtral-8x7B-shaped layer, prefill batch
+    "mixtral_prefill": LayerConfig("mixtral_prefill", T=4096, d=4096, N=8, k=2, d_ff=14336,
+                                   dtype="bf16", ffn=FFN_SWIGLU, gating=GATE_TOPK_SOFTMAX,
+                                   seed=1002),
+    # same layer, decode-sized batch
+    "mixtral_decode": LayerConfig("mixtral_decode", T=16, d=4096, N=8, k=2, d_ff=14336,
+                                  dtype="bf16", ffn=FFN_SWIGLU, gating=GATE_TOPK_SOFTMAX,
+                                  seed=1003),
+    # DeepSeek-V3-shaped fine-grained layer: 256 routed + 1 shared, top-8 of a full softmax
+    "deepseek_v3": LayerConfig("deepseek_v3", T=8192, d=7168, N=256, k=8, d_ff=2048,
+                               dtype="bf16", ffn=FFN_SWIGLU, gating=GATE_SOFTMAX_TOPK,
+                               has_shared=True, seed=1004),
+    # skewed routing with expert capacity ceil(2.0 * T * k / N)
+    "skewed_capacity": LayerConfig("skewed_capacity", T=16384, d=3584, N=128, k=2, d_ff=2560,
+                                   dtype="bf16", ffn=FFN_SWIGLU, gating=GATE_TOPK_SOFTMAX,
+                                   capacity_factor=2.0, zipf_bias=True, seed=1005),
+}
+
+
+def zipf_bias(N: int) -> torch.Tensor:
+    """b[e] = -2 ln(e + 1), drawn once in float64 and rounded to fp32."""
+    return torch.tensor([-2.0 * math.log(e + 1.0) for e in range(N)], dtype=torch.float64).float()
+
+
+def _gen(device: torch.device, seed: int, stream: int, expert: int = 0) -> torch.Generator:
+    g = torch.Generator(device=device)
+    # distinct, reproducible seed per (config, tensor, expert)
+    g.manual_seed(((seed * 1009 + stream) * 1000003 + expert) & 0x7FFFFFFFFFFFFFFF)
+    return g
+
+
+def _normal(shape, std: float, dtype: torch.dtype, device, gen) -> torch.Tensor:
+    v = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if std != 1.0:
+        v.mul_(std)
+    return v.to(dtype)
+
+
+def make_inputs(cfg: LayerConfig, device="cpu", experts: Optional[range] = None) -> Dict[str, torch.Tensor]:
+    """Draw every input of one layer call on `device`.
+
+    Returns a dict with x, w_router, logit_bias (or None), w_gate (None for
+    ReLU), w_up, w_down and, when cfg.has_shared, sh_gate, sh_up, sh_down.
+    Expert weights are drawn one expert at a time (bounded temporaries).
+    """
+    device = torch.device(device)
+    dt = cfg.torch_dtype
+    T, d, N, dff = cfg.T, cfg.d, cfg.N, cfg.d_ff
+    out: Dict[str, Optional[torch.Tensor]] = {}
+    out["x"] = _normal((T, d), 1.0, dt, device, _gen(device, cfg.seed, STREAM_X))
+    out["w_router"] = _normal((N, d), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_ROUTER))
+    out["logit_bias"] = zipf_bias(N).to(device) if cfg.zipf_bias else None
+
+    def expert_stack(stream, rows, cols, std):
+        w = torch.empty((N, rows, cols), dtype=dt, device=device)
+        for e in range(N):
+            w[e].copy_(_normal((rows, cols), std, dt, device, _gen(device, cfg.seed, stream, e)))
+        return w
+
+    out["w_gate"] = expert_stack(STREAM_GATE, dff, d, 1.0 / math.sqrt(d)) if cfg.ffn == FFN_SWIGLU else None
+    out["w_up"] = expert_stack(STREAM_UP, dff, d, 1.0 / math.sqrt(d))
+    out["w_down"] = expert_stack(STREAM_DOWN, d, dff, 1.0 / math.sqrt(dff))
+    if cfg.has_shared:
+        out["sh_gate"] = _normal((dff, d), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_SH_GATE))
+        out["sh_up"] = _normal((dff, d), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_SH_UP))
+        out["sh_down"] = _normal((d, dff), 1.0 / math.sqrt(dff), dt, device, _gen(device, cfg.seed, STREAM_SH_DOWN))
+    else:
+        out["sh_gate"] = out["sh_up"] = out["sh_down"] = None
+    return out
+
+
+def scaled(cfg: LayerConfig, **kw) -> LayerConfig:
+    """A copy of `cfg` with some sizes changed (parity cases at reduced sizes)."""
+    return cfg.replace(**kw)
