@@ -281,9 +281,9 @@ def forward(x, w_router, w_up, w_down, k: int, ffn: str, gating: str, w_gate=Non
         wg = w_gate[e] if ffn == SWIGLU else None
         slot_out[rows, slots, :] = expert_ffn(x[tok[rows]], w_up[e], w_down[e], ffn, wg)
     y_sh = None
-    if shared is not None:
+    if shared is not None:          # same FFN form as the routed experts
         sg, su, sd = shared
-        y_sh = expert_ffn(x[tok], su, sd, SWIGLU if sg is not None else RELU2, sg)
+        y_sh = expert_ffn(x[tok], su, sd, ffn, sg)
     y = combine(slot_out, w[tok], y_sh)
     return dict(z=z, idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, C=C, y=y,
                 y_shared=y_sh)

@@ -152,7 +152,8 @@ def make_inputs(cfg: LayerConfig, device="cpu", experts: Optional[range] = None)
     out["w_up"] = expert_stack(STREAM_UP, dff, d, 1.0 / math.sqrt(d))
     out["w_down"] = expert_stack(STREAM_DOWN, d, dff, 1.0 / math.sqrt(dff))
     if cfg.has_shared:
-        out["sh_gate"] = _normal((dff, d), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_SH_GATE))
+        out["sh_gate"] = (_normal((dff, d), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_SH_GATE))
+                          if cfg.ffn == FFN_SWIGLU else None)
         out["sh_up"] = _normal((dff, d), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_SH_UP))
         out["sh_down"] = _normal((d, dff), 1.0 / math.sqrt(dff), dt, device, _gen(device, cfg.seed, STREAM_SH_DOWN))
     else:
