@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixtral_prefill]
+
+A step is one whole layer forward (router, gating, grouping, expert FFNs,
+combine) over one resident batch of synthetic inputs.  Prints one JSON line:
+throughput in tokens/s over exactly K timed steps, the per-stage device
+times from HIP events recorded on the layer's stream, the roofline of the
+dominant kernel (the grouped gate/up projection; for decode-sized batches the
+bytes of the distinct experts it reads), and the CPU oracle timed on a bounded
+sample of the same layer.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (prefill); % HBM GB/s (decode)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded (same soname)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, ev: int) -> None:
+        self.hip.hipEventDestroy(ev)
+
+
+def algorithmic_counts(cfg, counts):
+    """Flops and bytes of one layer call by the definitions (not the implementation).
+
+    flops: router 2*T*d*N; per kept (token, expert) slot 2*nm*d*d_ff (nm = 3 SwiGLU, 2 ReLU);
+    the shared expert adds 2*nm*d*d_ff per token.  bytes: the weights of the distinct experts
+    touched (plus the shared expert), the router weights, x and y.
+    ffn_in: the gate/up (or W1) projection alone, per launch."""
+    import numpy as np
+    nm = 3 if cfg.ffn == "swiglu" else 2
+    nm_in = nm - 1
+    eb = cfg.elem_bytes
+    kept = int(np.sum(counts))
+    touched = int(np.sum(counts > 0))
+    rows_sh = cfg.T if cfg.has_shared else 0
+    flops = 2.0 * cfg.T * cfg.d * cfg.N + 2.0 * nm * cfg.d * cfg.d_ff * (kept + rows_sh)
+    w_expert = nm * cfg.d * cfg.d_ff * eb
+    bytes_ = (touched + (1 if cfg.has_shared else 0)) * w_expert + cfg.N * cfg.d * eb + 2 * cfg.T * cfg.d * eb
+    ffn_in_flops = 2.0 * nm_in * cfg.d * cfg.d_ff * (kept + rows_sh)
+    ffn_in_bytes = ((touched + (1 if cfg.has_shared else 0)) * nm_in * cfg.d * cfg.d_ff * eb
+                    + cfg.T * cfg.d * eb + (kept + rows_sh) * cfg.d_ff * eb)
+    return dict(flops=flops, bytes=bytes_, touched=touched, kept=kept,
+                ffn_in_flops=ffn_in_flops, ffn_in_bytes=ffn_in_bytes)
+
+
+def cpu_baseline(cfg, inp, sample_tokens: int):
+    """The float64 CPU oracle, as it stands, on the first `sample_tokens` tokens of the same layer
+    (same weights; the oracle reads each touched expert's weights once, converted to float64)."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    S = min(sample_tokens, cfg.T)
+
+    class View:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            return self.t[int(e)].float().cpu().numpy().astype(np.float64)
+
+    def f64(t):
+        return None if t is None else t.float().cpu().numpy().astype(np.float64)
+
+    t0 = time.perf_counter()
+    shared = (f64(inp["sh_gate"]), f64(inp["sh_up"]), f64(inp["sh_down"])) if cfg.has_shared else None
+    O.forward(f64(inp["x"][:S]), f64(inp["w_router"]), View(inp["w_up"]), View(inp["w_down"]), cfg.k,
+              O.SWIGLU if cfg.ffn == "swiglu" else O.RELU2,
+              O.TOPK_SOFTMAX if cfg.gating == "topk_softmax" else O.SOFTMAX_TOPK,
+              w_gate=View(inp["w_gate"]) if inp["w_gate"] is not None else None,
+              logit_bias=None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy(),
+              capacity_factor=cfg.capacity_factor, shared=shared)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer forward on the first {S} of {cfg.T} tokens (same layer and weights), float64, "
+                      f"{dt:.1f} s including the float64 conversion of each touched expert's weights"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_prefill")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU's share of the layer; --gpus {args.gpus} is not "
+              f"supported (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import mixture_experts_layer_48_amd as M
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    cfg = W.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    inp = W.make_inputs(cfg, "cuda")
+    desc = M.make_desc(cfg.T, cfg.d, cfg.N, cfg.k, cfg.d_ff, cfg.dtype, cfg.ffn, cfg.gating,
+                       cfg.capacity_factor, cfg.has_shared)
+    layer = M.MoELayer(desc, inp)
+    routing = layer.routing_buffers()
+    y = torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device="cuda")
+    hip = HipEvents()
+    nev = M.MOE_NUM_STAGES + 1
+
+    for _ in range(args.warmup):
+        layer.forward(inp["x"], y=y, out_routing=routing)
+    events = [[hip.create() for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer.forward(inp["x"], y=y, out_routing=routing, events=events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    stage_ms = [sum(hip.elapsed_ms(ev[s], ev[s + 1]) for ev in events) / args.steps
+                for s in range(M.MOE_NUM_STAGES)]
+    step_dev_ms = sum(hip.elapsed_ms(ev[0], ev[-1]) for ev in events) / args.steps
+    for ev in events:
+        for e in ev:
+            hip.destroy(e)
+
+    counts = routing["counts"].cpu().numpy()
+    alg = algorithmic_counts(cfg, counts)
+    tokens_per_s = cfg.T * args.steps / (t1 - t0)
+    ffn_in_ms = stage_ms[3]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ai = alg["ffn_in_flops"] / alg["ffn_in_bytes"]
+    if cfg.dtype == "f32":
+        roof = {"bound": "alu", "achieved": alg["ffn_in_flops"] / (ffn_in_ms * 1e-3) / 1e12,
+                "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
+    elif ai >= ridge:
+        roof = {"bound": "mfma", "achieved": alg["ffn_in_flops"] / (ffn_in_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": alg["ffn_in_bytes"] / (ffn_in_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "ffn_in (grouped gate/up projection)"
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian inputs and weights of the layer's shapes)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "N": cfg.N, "k": cfg.k, "d_ff": cfg.d_ff,
+                   "ffn": cfg.ffn, "gating": cfg.gating, "capacity_factor": cfg.capacity_factor,
+                   "shared_expert": cfg.has_shared},
+        "layer": {"tflops": alg["flops"] / (ms_per_step * 1e-3) / 1e12,
+                  "mfma_frac": alg["flops"] / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "gbs_distinct_experts": alg["bytes"] / (ms_per_step * 1e-3) / 1e9,
+                  "hbm_frac": alg["bytes"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "experts_touched": alg["touched"], "device_ms_per_step": step_dev_ms},
+        "stages_ms": dict(zip(M.STAGE_NAMES, stage_ms)),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        default_sample = {"tiny_fp32": 128, "mixtral_prefill": 256, "mixtral_decode": 16,
+                          "deepseek_v3": 64, "skewed_capacity": 512}.get(cfg.name, 64)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens or default_sample)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

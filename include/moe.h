@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of the sparse mixture-of-experts layer forward on MI355X (gfx950).
+ *
+ * One call computes, for one GPU holding every expert of the layer:
+ *   1. router logits      z = x W_r (+ b)
+ *   2. ranking + gating   top-k experts per token and their gate weights
+ *   3. expert capacity    optional per-expert cap with re-routing to the next-best expert
+ *   4. grouping by expert the (token, slot) pairs sorted into contiguous per-expert rows
+ *   5. expert FFNs        grouped over experts (SwiGLU or two-layer ReLU), plus an
+ *                         optional shared expert applied to every token
+ *   6. combine            gate-weighted sum of each token's k expert outputs
+ *
+ * Sources (web pages on MoE layers, cited by title and section):
+ *   [P1] "MoE 分片：混合專家模型的平行化策略" -- sections 什麼是 MoE 模型 (router is a learned
+ *        linear layer, only the top-k experts run, outputs weighted by the router's scores;
+ *        an expert is two linear maps around an activation) and 動態 token 路由 (steps 2
+ *        and 6: scoring, softmax, top-k; weighted combine on the token's own device).
+ *   [P2] "MoE 推理：激活参数 vs 总参数与专家路由" -- sections 深入原理 and 代码 (router linear,
+ *        top-k, softmax over the picked logits, weighted sum; decode reads the weights of the
+ *        distinct experts a batch touches).
+ *   [P3] "大模型MoE混合专家架构原理与DeepSeek-V4工程实践解析" -- section MoE核心机制 (softmax
+ *        over all experts, then top-K, outputs weighted by the un-renormalised probabilities).
+ *   [P4] "MoE 架构科普：为什么大模型要「混合专家」" -- section 专家粒度 (shared experts that
+ *        every token passes through).
+ *   [P5] "MoE稀疏激活原理与工程实践：揭秘大模型参数幻觉" -- section 2.2 (expert capacity:
+ *        a full expert sends the token to its next-best expert; capacity_factor 2.0) and
+ *        section 3.1 (tokens regrouped by target expert id before the experts run).
+ *
+ * Conventions
+ *  - All tensors are row-major and contiguous, on the device unless stated otherwise.
+ *  - Weights are stored output-major, one row per output feature (a linear layer's weight):
+ *      w_router [N, d]; w_gate, w_up [N, d_ff, d]; w_down [N, d, d_ff];
+ *      shared expert: sh_gate, sh_up [d_ff, d], sh_down [d, d_ff].
+ *    For MOE_FFN_RELU2, w_up holds W1 and w_down holds W2 (y = relu(x W1) W2); w_gate unused.
+ *  - Activations and weights share one dtype (MOE_F32 or MOE_BF16).  Logits, gate weights
+ *    and every accumulation are fp32; the router accumulates fp32 partial sums of 256
+ *    products each into fp64.  The FFN hidden state H is stored in the layer dtype (bf16
+ *    rounding to nearest even); the per-row expert outputs (y_perm) are fp32 for every layer
+ *    dtype, and the output y is rounded once, in the combine, to the layer dtype.
+ *  - Ownership: the caller owns every buffer, including the workspace sized by
+ *    moe_workspace_size().  The library allocates no device memory, keeps no pointer after a
+ *    call returns and holds no state across calls beyond the thread-local error text.
+ *  - Asynchrony: every compute call validates its arguments on the host, then only enqueues
+ *    kernels on `stream` (a hipStream_t; NULL = the default stream) and returns.  The host is
+ *    never synchronised.  On any error status nothing has been enqueued, except MOE_ERR_HIP,
+ *    which reports a failed launch (earlier kernels of that call may have been enqueued).
+ *  - Determinism: no floating-point atomics; every reduction has a fixed order, so equal
+ *    inputs give bit-identical outputs.
+ *  - Thread safety: calls may run concurrently if each uses its own workspace and outputs.
+ *  - NaN/Inf inputs are not checked; results are then undefined.
+ *
+ * Routing semantics (fixed readings where the pages are silent)
+ *  - Ranking: descending logit; equal logits rank the lower expert id first.
+ *  - idx[t, j] is the expert of token t's slot j; slot 0 is the best-ranked kept expert.
+ *  - MOE_GATE_TOPK_SOFTMAX: w = softmax over the logits of the k kept experts [P2].
+ *    MOE_GATE_SOFTMAX_TOPK: w_j = softmax over all N logits, taken at idx_j, no renormalisation [P3].
+ *  - Capacity (capacity_factor > 0): C = ceil(capacity_factor * T * k / N).  Slots are placed
+ *    in priority order: every token's slot 0 in token order, then every token's slot 1, ...
+ *    A slot takes the highest-ranked expert that the token does not already hold and whose
+ *    fill is still below C [P5 2.2].  A slot with no room anywhere is dropped: idx = -1,
+ *    w = 0, and it appears in no expert's rows.  Gate weights use the final experts' logits.
+ *  - The logit bias b (optional) is part of the logit for ranking and for the weights.
+ *  - Grouping: counts[e] = number of slots routed to e; offsets = exclusive prefix sum
+ *    (offsets[N] = kept slots); perm[r] = slot s = t*k + j held by row r, rows of expert e
+ *    ordered by ascending slot; inv[s] = row of slot s, or -1 if the slot was dropped.
+ *  - Shared expert (has_shared): applied to every token with weight 1; it is not counted in
+ *    counts.  In y_perm its output for token t sits at row T*k + t.
+ *
+ * Limits: 1 <= k <= N <= 256; T >= 0 (T = 0 is a no-op); d, d_ff >= 1.  For MOE_BF16:
+ *   d % 64 == 0 and d_ff % 64 == 0 (else MOE_ERR_UNSUPPORTED).  MOE_F32 has no divisibility
+ *   requirement.  T * k must fit in int32 with T*k + T + 1 < 2^31.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* null required pointer, size or enum out of range */
+    MOE_ERR_UNSUPPORTED = 2,   /* valid request this build cannot run (N > 256, d % 64 on bf16) */
+    MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than moe_workspace_size() or ws NULL */
+    MOE_ERR_HIP = 4            /* a HIP call or kernel launch failed; see moe_last_error() */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_GATE_TOPK_SOFTMAX = 0, MOE_GATE_SOFTMAX_TOPK = 1 } moe_gating;
+typedef enum { MOE_FFN_RELU2 = 0, MOE_FFN_SWIGLU = 1 } moe_ffn;
+
+/* hipStream_t, passed as an opaque handle (NULL = default stream). */
+typedef void *moe_stream_t;
+
+/* Shapes and options of one layer call (all fields by value, host memory). */
+typedef struct {
+    int32_t T;                 /* tokens (rows of x) */
+    int32_t d;                 /* model width */
+    int32_t N;                 /* routed experts */
+    int32_t k;                 /* experts per token */
+    int32_t d_ff;              /* expert hidden width */
+    int32_t dtype;             /* moe_dtype */
+    int32_t ffn;               /* moe_ffn */
+    int32_t gating;            /* moe_gating */
+    float capacity_factor;     /* <= 0: no capacity limit */
+    int32_t has_shared;        /* 1: one shared expert, weight 1, every token */
+} moe_layer_desc;
+
+/* Device pointers to the layer's weights (layouts in the header comment). */
+typedef struct {
+    const void *w_router;      /* [N, d] */
+    const float *logit_bias;   /* [N] fp32, or NULL */
+    const void *w_gate;        /* [N, d_ff, d]; NULL for MOE_FFN_RELU2 */
+    const void *w_up;          /* [N, d_ff, d] (W1 for RELU2) */
+    const void *w_down;        /* [N, d, d_ff] (W2 for RELU2) */
+    const void *sh_gate;       /* [d_ff, d] or NULL (required with has_shared and SWIGLU) */
+    const void *sh_up;         /* [d_ff, d] or NULL (required with has_shared) */
+    const void *sh_down;       /* [d, d_ff] or NULL (required with has_shared) */
+} moe_weights;
+
+/* Optional routing outputs of moe_layer_forward (device pointers; any may be NULL). */
+typedef struct {
+    float *logits;             /* [T, N] fp32 router logits (bias included) */
+    int32_t *idx;              /* [T, k] */
+    float *w;                  /* [T, k] */
+    int32_t *counts;           /* [N] */
+    int32_t *offsets;          /* [N + 1] */
+    int32_t *perm;             /* [T * k]; entries past offsets[N] are unspecified */
+    int32_t *inv;              /* [T * k] */
+} moe_routing;
+
+/* Number of pipeline stages whose boundaries moe_layer_forward_timed() marks:
+ * route | capacity | permute | ffn_in (gate/up or W1) | ffn_out (down or W2) | combine. */
+#define MOE_NUM_STAGES 6
+
+/* Bytes of device workspace a moe_layer_forward() call with this descriptor needs; the
+ * per-stage calls need at most as much.  Returns 0 for an invalid descriptor. */
+size_t moe_workspace_size(const moe_layer_desc *desc);
+
+/* Steps 1-3 [P1 步驟二, P2 深入原理, P3 MoE核心机制, P5 2.2]: router GEMM, ranking, gating
+ * and (if capacity_factor > 0) capacity routing.
+ *   x [T, d] (layer dtype); w_router [N, d]; logit_bias [N] fp32 or NULL.
+ *   logits [T, N] fp32 output or NULL; idx [T, k] int32 and w [T, k] fp32 outputs (required).
+ *   ws/ws_bytes: workspace of at least moe_workspace_size(desc) bytes. */
+moe_status moe_route(const moe_layer_desc *desc, const void *x, const void *w_router,
+                     const float *logit_bias, float *logits, int32_t *idx, float *w,
+                     void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Step 4 [P5 3.1]: stable grouping of the T*k slots by expert (idx -1 = dropped slot).
+ *   idx [T, k] in; counts [N], offsets [N + 1], perm [T * k], inv [T * k] out (required).
+ *   x [T, d] and x_perm [T * k, d]: optional (both or neither); when given, row r of x_perm
+ *   receives x[perm[r] / k] for r < offsets[N]. */
+moe_status moe_permute(const moe_layer_desc *desc, const int32_t *idx, int32_t *counts,
+                       int32_t *offsets, int32_t *perm, int32_t *inv, const void *x,
+                       void *x_perm, moe_stream_t stream);
+
+/* Steps 5 [P1 什麼是 MoE 模型, P4 专家粒度]: the expert FFNs, grouped over experts.
+ *   Row r < offsets[N] of expert e (offsets[e] <= r < offsets[e+1]) computes
+ *   FFN_e(x[perm[r] / k]) and, if row_scale is given, multiplies it by row_scale[perm[r]]
+ *   (the slot's gate weight, [T * k] fp32).  With has_shared, rows T*k .. T*k + T - 1 hold
+ *   the shared expert's output for tokens 0 .. T-1 (never scaled).
+ *   y_perm: [(T * k + (has_shared ? T : 0)), d] fp32; rows not listed above are left
+ *   untouched.  ws: workspace (hidden state H). */
+moe_status moe_expert_ffn(const moe_layer_desc *desc, const moe_weights *weights,
+                          const void *x, const int32_t *perm, const int32_t *offsets,
+                          const float *row_scale, void *y_perm, void *ws, size_t ws_bytes,
+                          moe_stream_t stream);
+
+/* Step 6 [P1 步驟六, P2 代码]: y[t] = sum_j s_j * y_perm[inv[t*k + j]] (+ y_perm[T*k + t] with
+ * has_shared), summed in slot order in fp32 and rounded once to the layer dtype;
+ * s_j = w[t, j] if w is not NULL, else 1 (rows already scaled).  Dropped slots are skipped.
+ *   y_perm (fp32) as produced by moe_expert_ffn; inv [T * k]; w [T, k] or NULL; y [T, d] out
+ *   in the layer dtype. */
+moe_status moe_combine(const moe_layer_desc *desc, const void *y_perm, const int32_t *inv,
+                       const float *w, void *y, moe_stream_t stream);
+
+/* The whole layer (steps 1-6) in one call.  y [T, d] out.  routing: optional copies of the
+ * routing tensors (NULL = not wanted). */
+moe_status moe_layer_forward(const moe_layer_desc *desc, const moe_weights *weights,
+                             const void *x, void *y, const moe_routing *routing,
+                             void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* As moe_layer_forward, and additionally records hipEvent_t events[i] (caller-created,
+ * i = 0 .. MOE_NUM_STAGES, so MOE_NUM_STAGES + 1 events) on `stream` before the first stage
+ * and after each stage, so that hipEventElapsedTime(events[i], events[i+1]) is stage i's
+ * device time.  A stage that does not apply (capacity without a limit) has zero length.
+ * events may be NULL (then this is moe_layer_forward). */
+moe_status moe_layer_forward_timed(const moe_layer_desc *desc, const moe_weights *weights,
+                                   const void *x, void *y, const moe_routing *routing,
+                                   void *ws, size_t ws_bytes, moe_stream_t stream,
+                                   void *const *events);
+
+/* Static text of a status code. */
+const char *moe_status_str(moe_status s);
+/* Detail of the last error on the calling thread ("" if none). */
+const char *moe_last_error(void);
+/* Library version string. */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,213 @@
+"""Python binding of libmoe.so, the MI355X (gfx950) sparse MoE layer forward.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current HIP stream.  The
+functions keep the C ABI's names (include/moe.h) and raise MoeError on any
+status other than MOE_OK.  If libmoe.so has not been built this module still
+imports, but every call raises (there is no other code path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_GATE_TOPK_SOFTMAX, MOE_GATE_SOFTMAX_TOPK = 0, 1
+MOE_FFN_RELU2, MOE_FFN_SWIGLU = 0, 1
+MOE_NUM_STAGES = 6
+STAGE_NAMES = ("route", "capacity", "permute", "ffn_in", "ffn_out", "combine")
+
+_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16}
+_FFNS = {"relu2": MOE_FFN_RELU2, "swiglu": MOE_FFN_SWIGLU}
+_GATINGS = {"topk_softmax": MOE_GATE_TOPK_SOFTMAX, "softmax_topk": MOE_GATE_SOFTMAX_TOPK}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func}: {_status_name(status)}: {detail}")
+
+
+class moe_layer_desc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("gating", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float), ("has_shared", ctypes.c_int32)]
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_router", "logit_bias", "w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")]
+
+
+class moe_routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("logits", "idx", "w", "counts", "offsets", "perm", "inv")]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def _status_name(s: int) -> str:
+    names = ["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"]
+    return names[s] if 0 <= s < len(names) else f"status {s}"
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m mixture_experts_layer_48_amd.build`")
+    # torch first: its HIP runtime (same soname) is then the one libmoe.so binds to, so streams
+    # and device pointers from torch are valid in the library
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    pdesc = ctypes.POINTER(moe_layer_desc)
+    lib.moe_workspace_size.argtypes = [pdesc]
+    lib.moe_workspace_size.restype = sz
+    lib.moe_route.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_permute.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_expert_ffn.argtypes = [pdesc, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_combine.argtypes = [pdesc, vp, vp, vp, vp, vp]
+    lib.moe_layer_forward.argtypes = [pdesc, ctypes.POINTER(moe_weights), vp, vp,
+                                      ctypes.POINTER(moe_routing), vp, sz, vp]
+    lib.moe_layer_forward_timed.argtypes = [pdesc, ctypes.POINTER(moe_weights), vp, vp,
+                                            ctypes.POINTER(moe_routing), vp, sz, vp, ctypes.POINTER(vp)]
+    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+              "moe_layer_forward_timed"):
+        getattr(lib, f).restype = i32
+    lib.moe_status_str.argtypes = [i32]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_version.argtypes = []
+    lib.moe_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, func: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, func, load_library().moe_last_error().decode())
+
+
+def make_desc(T: int, d: int, N: int, k: int, d_ff: int, dtype: str = "bf16", ffn: str = "swiglu",
+              gating: str = "topk_softmax", capacity_factor: float = 0.0, has_shared: bool = False) -> moe_layer_desc:
+    return moe_layer_desc(T, d, N, k, d_ff, _DTYPES.get(dtype, dtype), _FFNS.get(ffn, ffn),
+                          _GATINGS.get(gating, gating), float(capacity_factor), int(bool(has_shared)))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _weights(w: Dict) -> moe_weights:
+    return moe_weights(*(_ptr(w.get(n)) for n in
+                         ("w_router", "logit_bias", "w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")))
+
+
+# ---------------------------------------------------------------- the C ABI, one to one
+def moe_workspace_size(desc: moe_layer_desc) -> int:
+    return int(load_library().moe_workspace_size(ctypes.byref(desc)))
+
+
+def moe_route(desc, x, w_router, logit_bias, logits, idx, w, ws, stream=None) -> None:
+    _check(load_library().moe_route(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(logits),
+                                    _ptr(idx), _ptr(w), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream)), "moe_route")
+
+
+def moe_permute(desc, idx, counts, offsets, perm, inv, x=None, x_perm=None, stream=None) -> None:
+    _check(load_library().moe_permute(ctypes.byref(desc), _ptr(idx), _ptr(counts), _ptr(offsets), _ptr(perm),
+                                      _ptr(inv), _ptr(x), _ptr(x_perm), _stream(stream)), "moe_permute")
+
+
+def moe_expert_ffn(desc, weights: Dict, x, perm, offsets, row_scale, y_perm, ws, stream=None) -> None:
+    wt = _weights(weights)
+    _check(load_library().moe_expert_ffn(ctypes.byref(desc), ctypes.byref(wt), _ptr(x), _ptr(perm), _ptr(offsets),
+                                         _ptr(row_scale), _ptr(y_perm), _ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_combine(desc, y_perm, inv, w, y, stream=None) -> None:
+    _check(load_library().moe_combine(ctypes.byref(desc), _ptr(y_perm), _ptr(inv), _ptr(w), _ptr(y),
+                                      _stream(stream)), "moe_combine")
+
+
+def moe_layer_forward(desc, weights: Dict, x, y, routing: Optional[Dict] = None, ws=None, stream=None,
+                      events: Optional[Sequence[int]] = None) -> None:
+    """The whole layer; `events` (MOE_NUM_STAGES + 1 hipEvent_t handles) selects the timed entry point."""
+    lib = load_library()
+    wt = _weights(weights)
+    r = moe_routing(*(_ptr((routing or {}).get(n)) for n in
+                      ("logits", "idx", "w", "counts", "offsets", "perm", "inv")))
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if events is None:
+        st = lib.moe_layer_forward(ctypes.byref(desc), ctypes.byref(wt), _ptr(x), _ptr(y), ctypes.byref(r),
+                                   _ptr(ws), ws_bytes, _stream(stream))
+        _check(st, "moe_layer_forward")
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        st = lib.moe_layer_forward_timed(ctypes.byref(desc), ctypes.byref(wt), _ptr(x), _ptr(y), ctypes.byref(r),
+                                         _ptr(ws), ws_bytes, _stream(stream), arr)
+        _check(st, "moe_layer_forward_timed")
+
+
+# ---------------------------------------------------------------- convenience
+class MoELayer:
+    """One layer's descriptor, weights (device tensors in the ABI layouts) and workspace.
+
+    forward(x) enqueues moe_layer_forward on the current stream and returns
+    y plus, if routing=True, the routing tensors (logits, idx, w, counts,
+    offsets, perm, inv)."""
+
+    def __init__(self, desc: moe_layer_desc, weights: Dict, device=None):
+        import torch
+        self.desc = desc
+        self.weights = weights
+        ref = weights["w_up"]
+        self.device = device or ref.device
+        self.dtype = ref.dtype
+        nbytes = moe_workspace_size(desc)
+        if nbytes == 0:
+            _check(MOE_ERR_INVALID_ARG, "moe_workspace_size")
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+
+    def routing_buffers(self) -> Dict:
+        import torch
+        T, N, k = self.desc.T, self.desc.N, self.desc.k
+        dev = self.device
+        return dict(logits=torch.empty((T, N), dtype=torch.float32, device=dev),
+                    idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+                    w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                    counts=torch.empty(N, dtype=torch.int32, device=dev),
+                    offsets=torch.empty(N + 1, dtype=torch.int32, device=dev),
+                    perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+                    inv=torch.empty(T * k, dtype=torch.int32, device=dev))
+
+    def forward(self, x, routing: bool = False, y=None, out_routing: Optional[Dict] = None, events=None):
+        import torch
+        if y is None:
+            y = torch.empty((self.desc.T, self.desc.d), dtype=self.dtype, device=self.device)
+        r = out_routing if out_routing is not None else (self.routing_buffers() if routing else None)
+        moe_layer_forward(self.desc, self.weights, x, y, r, self.ws, events=events)
+        return (y, r) if r is not None else y

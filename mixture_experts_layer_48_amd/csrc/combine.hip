@@ -1,0 +1,80 @@
+// Step 6 of the MoE layer: the gate-weighted combine.  Each token's output is the sum of its k
+// expert outputs weighted by the router's gate weights (page "MoE 分片：混合專家模型的平行化策略",
+// section 動態 token 路由, step 6; page "MoE 推理：激活参数 vs 总参数与专家路由", section 代码),
+// plus the shared expert's output with weight 1 when the layer has one.
+//
+// One block per token; the fp32 expert rows are summed in slot order in fp32 and the result is
+// rounded once to the layer dtype, so the output does not depend on scheduling.
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(const float* __restrict__ yp,
+                                                           const int32_t* __restrict__ inv,
+                                                           const float* __restrict__ w,
+                                                           bf16* __restrict__ y, int T, int k, int d,
+                                                           int has_shared) {
+    const int t = blockIdx.x;
+    const int32_t* iv = inv + (size_t)t * k;
+    const float* wv = w ? w + (size_t)t * k : nullptr;
+    const float* ysh = yp + ((size_t)T * k + t) * d;
+    for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < k; ++j) {
+            const int r = iv[j];
+            if (r < 0) continue;
+            const float s = wv ? wv[j] : 1.0f;
+            const f32x4 v0 = *(const f32x4*)(yp + (size_t)r * d + c);
+            const f32x4 v1 = *(const f32x4*)(yp + (size_t)r * d + c + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i] = fmaf(s, v0[i], acc[i]);
+                acc[i + 4] = fmaf(s, v1[i], acc[i + 4]);
+            }
+        }
+        if (has_shared) {
+            const f32x4 v0 = *(const f32x4*)(ysh + c);
+            const f32x4 v1 = *(const f32x4*)(ysh + c + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i] += v0[i];
+                acc[i + 4] += v1[i];
+            }
+        }
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (bf16)acc[i];
+        *(bf16x8*)(y + (size_t)t * d + c) = o;
+    }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ yp,
+                                                          const int32_t* __restrict__ inv,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ y, int T, int k, int d,
+                                                          int has_shared) {
+    const int t = blockIdx.x;
+    const int32_t* iv = inv + (size_t)t * k;
+    const float* wv = w ? w + (size_t)t * k : nullptr;
+    for (int c = threadIdx.x; c < d; c += blockDim.x) {
+        float acc = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int r = iv[j];
+            if (r < 0) continue;
+            acc = fmaf(wv ? wv[j] : 1.0f, yp[(size_t)r * d + c], acc);
+        }
+        if (has_shared) acc += yp[((size_t)T * k + t) * d + c];
+        y[(size_t)t * d + c] = acc;
+    }
+}
+
+hipError_t launch_combine(const void* y_perm, const int32_t* inv, const float* w, void* y, int T,
+                          int k, int d, int has_shared, int dtype, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (dtype == 1)
+        hipLaunchKernelGGL(combine_bf16_kernel, dim3(T), dim3(256), 0, s, (const float*)y_perm, inv, w,
+                           (bf16*)y, T, k, d, has_shared);
+    else
+        hipLaunchKernelGGL(combine_f32_kernel, dim3(T), dim3(256), 0, s, (const float*)y_perm, inv, w,
+                           (float*)y, T, k, d, has_shared);
+    return hipGetLastError();
+}

@@ -1,0 +1,300 @@
+// C ABI of the MoE layer library: argument validation, workspace carving and the launch
+// sequence of each step.  Every entry point checks all of its arguments on the host before it
+// enqueues anything, never synchronises, never allocates and keeps no pointer after returning.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+moe_status hip_fail(hipError_t e, const char* where) {
+    g_err = std::string(where) + ": " + hipGetErrorString(e);
+    return MOE_ERR_HIP;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t elem_bytes(const moe_layer_desc& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
+bool has_capacity(const moe_layer_desc& d) { return d.capacity_factor > 0.0f; }
+long long rows_total(const moe_layer_desc& d) {
+    return (long long)d.T * d.k + (d.has_shared ? d.T : 0);
+}
+
+// Expert capacity C = ceil(capacity_factor * T * k / N), clamped to int range.
+int capacity_of(const moe_layer_desc& d) {
+    const double c = std::ceil((double)d.capacity_factor * (double)d.T * (double)d.k / (double)d.N);
+    return c >= (double)INT_MAX ? INT_MAX : (int)c;
+}
+
+moe_status check_desc(const moe_layer_desc* d) {
+    if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+    if (d->T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+    if (d->d < 1 || d->d_ff < 1) return fail(MOE_ERR_INVALID_ARG, "d and d_ff must be >= 1");
+    if (d->N < 1) return fail(MOE_ERR_INVALID_ARG, "N must be >= 1");
+    if (d->k < 1 || d->k > d->N) return fail(MOE_ERR_INVALID_ARG, "k must satisfy 1 <= k <= N");
+    if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+    if (d->ffn != MOE_FFN_RELU2 && d->ffn != MOE_FFN_SWIGLU) return fail(MOE_ERR_INVALID_ARG, "unknown ffn");
+    if (d->gating != MOE_GATE_TOPK_SOFTMAX && d->gating != MOE_GATE_SOFTMAX_TOPK)
+        return fail(MOE_ERR_INVALID_ARG, "unknown gating");
+    if (d->has_shared != 0 && d->has_shared != 1) return fail(MOE_ERR_INVALID_ARG, "has_shared must be 0 or 1");
+    if (std::isnan(d->capacity_factor) || std::isinf(d->capacity_factor))
+        return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
+    if (d->N > 256) return fail(MOE_ERR_UNSUPPORTED, "N > 256 experts");
+    if (d->dtype == MOE_BF16 && (d->d % 64 != 0 || d->d_ff % 64 != 0))
+        return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need d % 64 == 0 and d_ff % 64 == 0");
+    if ((long long)d->T * d->k + d->T + 1 >= (long long)INT_MAX)
+        return fail(MOE_ERR_UNSUPPORTED, "T*k + T exceeds int32 row indexing");
+    if ((long long)d->T * d->d >= (long long)INT_MAX * 64LL)
+        return fail(MOE_ERR_UNSUPPORTED, "T*d too large");
+    return MOE_OK;
+}
+
+moe_status check_weights(const moe_layer_desc& d, const moe_weights* w, bool need_router, bool need_ffn) {
+    if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+    if (need_router && !w->w_router) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
+    if (need_ffn) {
+        if (!w->w_up || !w->w_down) return fail(MOE_ERR_INVALID_ARG, "w_up / w_down is NULL");
+        if (d.ffn == MOE_FFN_SWIGLU && !w->w_gate) return fail(MOE_ERR_INVALID_ARG, "w_gate is NULL (SwiGLU)");
+        if (d.has_shared) {
+            if (!w->sh_up || !w->sh_down) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are NULL");
+            if (d.ffn == MOE_FFN_SWIGLU && !w->sh_gate) return fail(MOE_ERR_INVALID_ARG, "sh_gate is NULL");
+        }
+    }
+    return MOE_OK;
+}
+
+// Workspace of the whole forward, carved in this order (each piece 256-byte aligned).
+struct Layout {
+    size_t z, ranked, idx, w, counts, offsets, perm, inv, h, yp, total;
+};
+Layout layout_of(const moe_layer_desc& d) {
+    Layout L{};
+    size_t o = 0;
+    const size_t T = (size_t)d.T, N = (size_t)d.N, k = (size_t)d.k;
+    L.z = o; o += align256(T * N * 4);
+    L.ranked = o; o += has_capacity(d) ? align256(T * N) : 0;
+    L.idx = o; o += align256(T * k * 4);
+    L.w = o; o += align256(T * k * 4);
+    L.counts = o; o += align256(N * 4);
+    L.offsets = o; o += align256((N + 1) * 4);
+    L.perm = o; o += align256(T * k * 4);
+    L.inv = o; o += align256(T * k * 4);
+    L.h = o; o += align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d));
+    L.yp = o; o += align256((size_t)rows_total(d) * d.d * 4);  // fp32 expert rows
+    L.total = o;
+    return L;
+}
+size_t route_ws_bytes(const moe_layer_desc& d, bool have_logits) {
+    return (have_logits ? 0 : align256((size_t)d.T * d.N * 4)) +
+           (has_capacity(d) ? align256((size_t)d.T * d.N) : 0);
+}
+size_t ffn_ws_bytes(const moe_layer_desc& d) {
+    return align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d));
+}
+
+char* at(void* ws, size_t off) { return (char*)ws + off; }
+
+// ---- stages (arguments already validated)
+moe_status stage_route(const moe_layer_desc& d, const void* x, const void* wr, const float* bias, float* z,
+                       uint8_t* ranked, int32_t* idx, float* w, hipStream_t s, hipEvent_t ev_mid) {
+    hipError_t e = launch_router_logits(x, wr, bias, z, d.T, d.d, d.N, d.dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "router logits launch");
+    if (!has_capacity(d)) {
+        e = launch_topk_gate(z, d.T, d.N, d.k, d.gating, idx, w, s);
+        if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    }
+    if (ev_mid) {
+        e = hipEventRecord(ev_mid, s);
+        if (e != hipSuccess) return hip_fail(e, "event record");
+    }
+    if (has_capacity(d)) {
+        e = launch_capacity(z, ranked, d.T, d.N, d.k, capacity_of(d), d.gating, idx, w, s);
+        if (e != hipSuccess) return hip_fail(e, "capacity launch");
+    }
+    return MOE_OK;
+}
+
+FfnLaunch ffn_args(const moe_layer_desc& d, const moe_weights& wt, const void* x, const int32_t* perm,
+                   const int32_t* offsets, const float* row_scale, void* h, void* yp) {
+    FfnLaunch f{};
+    f.T = d.T; f.d = d.d; f.N = d.N; f.k = d.k; f.d_ff = d.d_ff;
+    f.dtype = d.dtype; f.ffn = d.ffn; f.has_shared = d.has_shared;
+    f.x = x; f.perm = perm; f.offsets = offsets;
+    f.w_gate = wt.w_gate; f.w_up = wt.w_up; f.w_down = wt.w_down;
+    f.sh_gate = wt.sh_gate; f.sh_up = wt.sh_up; f.sh_down = wt.sh_down;
+    f.row_scale = row_scale; f.h = h; f.y_perm = yp;
+    return f;
+}
+
+moe_status record(hipEvent_t ev, hipStream_t s) {
+    if (!ev) return MOE_OK;
+    hipError_t e = hipEventRecord(ev, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "event record");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_layer_desc* desc) {
+    if (check_desc(desc) != MOE_OK) return 0;
+    return layout_of(*desc).total;
+}
+
+moe_status moe_route(const moe_layer_desc* desc, const void* x, const void* w_router,
+                     const float* logit_bias, float* logits, int32_t* idx, float* w, void* ws,
+                     size_t ws_bytes, moe_stream_t stream) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const moe_layer_desc& d = *desc;
+    if (d.T == 0) return MOE_OK;
+    if (!x || !w_router || !idx || !w) return fail(MOE_ERR_INVALID_ARG, "x, w_router, idx and w are required");
+    const size_t need = route_ws_bytes(d, logits != nullptr);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(MOE_ERR_WORKSPACE, "workspace too small for moe_route: need " + std::to_string(need));
+    size_t o = 0;
+    float* z = logits;
+    if (!z) { z = (float*)at(ws, o); o += align256((size_t)d.T * d.N * 4); }
+    uint8_t* ranked = has_capacity(d) ? (uint8_t*)at(ws, o) : nullptr;
+    return stage_route(d, x, w_router, logit_bias, z, ranked, idx, w, (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_permute(const moe_layer_desc* desc, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, int32_t* inv, const void* x, void* x_perm, moe_stream_t stream) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const moe_layer_desc& d = *desc;
+    if (d.T == 0) return MOE_OK;
+    if (!idx || !counts || !offsets || !perm || !inv)
+        return fail(MOE_ERR_INVALID_ARG, "idx, counts, offsets, perm and inv are required");
+    if ((x == nullptr) != (x_perm == nullptr)) return fail(MOE_ERR_INVALID_ARG, "give both x and x_perm or neither");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_permute(idx, d.T, d.k, d.N, counts, offsets, perm, inv, s);
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    if (x_perm) {
+        e = launch_gather_rows(x, perm, offsets, d.T, d.k, d.N, (int)(d.d * elem_bytes(d)), x_perm, s);
+        if (e != hipSuccess) return hip_fail(e, "gather launch");
+    }
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
+                          const int32_t* perm, const int32_t* offsets, const float* row_scale, void* y_perm,
+                          void* ws, size_t ws_bytes, moe_stream_t stream) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const moe_layer_desc& d = *desc;
+    st = check_weights(d, weights, false, true);
+    if (st != MOE_OK) return st;
+    if (d.T == 0) return MOE_OK;
+    if (!x || !perm || !offsets || !y_perm) return fail(MOE_ERR_INVALID_ARG, "x, perm, offsets and y_perm are required");
+    const size_t need = ffn_ws_bytes(d);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace too small for moe_expert_ffn: need " + std::to_string(need));
+    hipStream_t s = (hipStream_t)stream;
+    FfnLaunch f = ffn_args(d, *weights, x, perm, offsets, row_scale, ws, y_perm);
+    hipError_t e = launch_ffn_in(f, s);
+    if (e != hipSuccess) return hip_fail(e, "ffn in-projection launch");
+    e = launch_ffn_out(f, s);
+    if (e != hipSuccess) return hip_fail(e, "ffn out-projection launch");
+    return MOE_OK;
+}
+
+moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int32_t* inv, const float* w,
+                       void* y, moe_stream_t stream) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const moe_layer_desc& d = *desc;
+    if (d.T == 0) return MOE_OK;
+    if (!y_perm || !inv || !y) return fail(MOE_ERR_INVALID_ARG, "y_perm, inv and y are required");
+    hipError_t e = launch_combine(y_perm, inv, w, y, d.T, d.k, d.d, d.has_shared, d.dtype, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
+}
+
+moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
+                                   void* y, const moe_routing* routing, void* ws, size_t ws_bytes,
+                                   moe_stream_t stream, void* const* events) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const moe_layer_desc& d = *desc;
+    st = check_weights(d, weights, true, true);
+    if (st != MOE_OK) return st;
+    if (d.T == 0) return MOE_OK;
+    if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x and y are required");
+    if (events)
+        for (int i = 0; i <= MOE_NUM_STAGES; ++i)
+            if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events array holds a NULL event");
+    const Layout L = layout_of(d);
+    if (!ws || ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE, "workspace too small for moe_layer_forward: need " + std::to_string(L.total));
+    hipStream_t s = (hipStream_t)stream;
+    auto ev = [&](int i) -> hipEvent_t { return events ? (hipEvent_t)events[i] : nullptr; };
+    const moe_routing none{};
+    const moe_routing& R = routing ? *routing : none;
+    float* z = R.logits ? R.logits : (float*)at(ws, L.z);
+    int32_t* idx = R.idx ? R.idx : (int32_t*)at(ws, L.idx);
+    float* w = R.w ? R.w : (float*)at(ws, L.w);
+    int32_t* counts = R.counts ? R.counts : (int32_t*)at(ws, L.counts);
+    int32_t* offsets = R.offsets ? R.offsets : (int32_t*)at(ws, L.offsets);
+    int32_t* perm = R.perm ? R.perm : (int32_t*)at(ws, L.perm);
+    int32_t* inv = R.inv ? R.inv : (int32_t*)at(ws, L.inv);
+    void* h = at(ws, L.h);
+    void* yp = at(ws, L.yp);
+
+    if ((st = record(ev(0), s)) != MOE_OK) return st;
+    st = stage_route(d, x, weights->w_router, weights->logit_bias, z, (uint8_t*)at(ws, L.ranked), idx, w, s, ev(1));
+    if (st != MOE_OK) return st;
+    if ((st = record(ev(2), s)) != MOE_OK) return st;
+    hipError_t e = launch_permute(idx, d.T, d.k, d.N, counts, offsets, perm, inv, s);
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    if ((st = record(ev(3), s)) != MOE_OK) return st;
+    FfnLaunch f = ffn_args(d, *weights, x, perm, offsets, w, h, yp);
+    e = launch_ffn_in(f, s);
+    if (e != hipSuccess) return hip_fail(e, "ffn in-projection launch");
+    if ((st = record(ev(4), s)) != MOE_OK) return st;
+    e = launch_ffn_out(f, s);
+    if (e != hipSuccess) return hip_fail(e, "ffn out-projection launch");
+    if ((st = record(ev(5), s)) != MOE_OK) return st;
+    e = launch_combine(yp, inv, nullptr, y, d.T, d.k, d.d, d.has_shared, d.dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return record(ev(6), s);
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_weights* weights, const void* x, void* y,
+                             const moe_routing* routing, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    return moe_layer_forward_timed(desc, weights, x, y, routing, ws, ws_bytes, stream, nullptr);
+}
+
+const char* moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Host-side launchers of the MoE kernels (one per .hip file group).  All enqueue on `s` and
+// return the launch status; none synchronises.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, float* z, int T,
+                                int d, int N, int dtype, hipStream_t s);
+hipError_t launch_topk_gate(const float* z, int T, int N, int k, int gating, int32_t* idx, float* w,
+                            hipStream_t s);
+hipError_t launch_capacity(const float* z, uint8_t* ranked, int T, int N, int k, int C, int gating,
+                           int32_t* idx, float* w, hipStream_t s);
+hipError_t launch_permute(const int32_t* idx, int T, int k, int N, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, const int32_t* perm, const int32_t* offsets, int T,
+                              int k, int N, int row_bytes, void* x_perm, hipStream_t s);
+
+// Grouped expert FFN.  Segment e < N: rows offsets[e] .. offsets[e+1]-1, weights of expert e;
+// segment N (has_shared): rows T*k .. T*k+T-1, the shared expert's weights.
+struct FfnLaunch {
+    int T, d, N, k, d_ff, dtype, ffn, has_shared;
+    const void* x;            // [T, d]
+    const int32_t* perm;      // [T*k]
+    const int32_t* offsets;   // [N+1]
+    const void* w_gate;       // [N, d_ff, d] or null
+    const void* w_up;         // [N, d_ff, d]
+    const void* w_down;       // [N, d, d_ff]
+    const void* sh_gate;      // [d_ff, d] or null
+    const void* sh_up;
+    const void* sh_down;
+    const float* row_scale;   // [T*k] or null
+    void* h;                  // [T*k + T, d_ff] hidden state
+    void* y_perm;             // [T*k + T, d]
+};
+hipError_t launch_ffn_in(const FfnLaunch& a, hipStream_t s);   // H = act(x W_in)
+hipError_t launch_ffn_out(const FfnLaunch& a, hipStream_t s);  // y_perm = scale * H W_out
+hipError_t launch_combine(const void* y_perm, const int32_t* inv, const float* w, void* y, int T,
+                          int k, int d, int has_shared, int dtype, hipStream_t s);

@@ -1,0 +1,134 @@
+// Step 4 of the MoE layer: group the (token, slot) pairs by target expert so that each expert
+// sees one contiguous block of rows (page "MoE稀疏激活原理与工程实践：揭秘大模型参数幻觉",
+// section 3.1: tokens routed one by one, then regrouped by expert id before the experts run).
+//
+// One block of 1024 threads does the whole grouping, deterministically and without atomics on
+// the output order:
+//   1. each wave counts its contiguous range of slots per expert (LDS histogram per wave);
+//   2. counts, the exclusive scan over experts (offsets) and each wave's starting row per
+//      expert (offsets[e] + counts of e in earlier waves);
+//   3. each wave walks its range again in groups of 64 slots, in order; a lane's row is its
+//      wave's next free row for its expert plus the number of lower lanes with the same expert
+//      (ballot matching), so rows of an expert are in ascending slot order.
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+#define PM_THREADS 1024
+#define PM_WAVES (PM_THREADS / 64)
+
+__global__ __launch_bounds__(PM_THREADS) void permute_kernel(
+    const int32_t* __restrict__ idx, int S, int N, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ int hist[PM_WAVES][MOE_MAX_EXPERTS];
+    __shared__ int offs[MOE_MAX_EXPERTS + 1];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // equal contiguous ranges per wave, a multiple of 64 slots each
+    const int per_wave = ((S + PM_WAVES * 64 - 1) / (PM_WAVES * 64)) * 64;
+    const int beg = wave * per_wave;
+    const int end = min(S, beg + per_wave);
+
+    for (int i = tid; i < PM_WAVES * MOE_MAX_EXPERTS; i += PM_THREADS) (&hist[0][0])[i] = 0;
+    __syncthreads();
+    for (int s = beg + lane; s < end; s += 64) {
+        const int e = idx[s];
+        if (e >= 0) atomicAdd(&hist[wave][e], 1);  // integer counts: order-independent
+    }
+    __syncthreads();
+    if (tid < 64) {  // one wave: totals, exclusive scan over experts
+        int tot[4], run = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid * 4 + q;
+            int c = 0;
+            if (e < N)
+                for (int ww = 0; ww < PM_WAVES; ++ww) c += hist[ww][e];
+            tot[q] = c;
+            run += c;
+        }
+        // inclusive scan of per-lane sums across the wave
+        int incl = run;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (tid >= o) incl += v;
+        }
+        int base = incl - run;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid * 4 + q;
+            if (e < N) {
+                offs[e] = base;
+                counts[e] = tot[q];
+                offsets[e] = base;
+            }
+            base += tot[q];
+        }
+        if (tid == 63) {
+            offs[N] = incl;
+            offsets[N] = incl;
+        }
+    }
+    __syncthreads();
+    // per-wave starting row of each expert: offsets[e] + counts of e in earlier waves
+    for (int e = tid; e < N; e += PM_THREADS) {
+        int run = offs[e];
+        for (int ww = 0; ww < PM_WAVES; ++ww) {
+            const int c = hist[ww][e];
+            hist[ww][e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (int g = 0; g < per_wave; g += 64) {
+        const int s = beg + g + lane;
+        const bool valid = s < end;
+        const int e = valid ? idx[s] : -1;
+        const uint64_t eq = match_lanes<9>((uint32_t)(e + 1));
+        const uint64_t lt = lanemask_lt();
+        if (e >= 0) {
+            const int r = hist[wave][e] + __popcll(eq & lt);
+            perm[r] = s;
+            inv[s] = r;
+        } else if (valid) {
+            inv[s] = -1;
+        }
+        __syncthreads();  // all reads of hist done before the group's update
+        if (e >= 0 && (eq & ~(lt | (1ull << lane))) == 0)  // highest lane of its group
+            hist[wave][e] += __popcll(eq);
+        __syncthreads();
+    }
+}
+
+// Optional materialised gather: x_perm[r] = x[perm[r] / k] for r < offsets[N].
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ x,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ offsets, int N,
+                                                          int k, int row_bytes, uint8_t* __restrict__ xp) {
+    const int r = blockIdx.x;
+    if (r >= offsets[N]) return;
+    const int t = perm[r] / k;
+    if ((row_bytes & 15) == 0) {  // every row starts 16-byte aligned
+        const u32x4* src = (const u32x4*)(x + (size_t)t * row_bytes);
+        u32x4* dst = (u32x4*)(xp + (size_t)r * row_bytes);
+        for (int i = threadIdx.x; i < row_bytes / 16; i += blockDim.x) dst[i] = src[i];
+    } else {
+        for (int i = threadIdx.x; i < row_bytes; i += blockDim.x)
+            xp[(size_t)r * row_bytes + i] = x[(size_t)t * row_bytes + i];
+    }
+}
+
+hipError_t launch_permute(const int32_t* idx, int T, int k, int N, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, hipStream_t s) {
+    const int S = T * k;
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PM_THREADS), 0, s, idx, S, N, counts, offsets,
+                       perm, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* perm, const int32_t* offsets, int T,
+                              int k, int N, int row_bytes, void* x_perm, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(T * k), dim3(256), 0, s, (const uint8_t*)x, perm,
+                       offsets, N, k, row_bytes, (uint8_t*)x_perm);
+    return hipGetLastError();
+}
