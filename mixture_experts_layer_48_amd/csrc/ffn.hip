@@ -16,13 +16,12 @@
 // SwiGLU (silu(g) * u) or ReLU is applied in registers and H is stored in bf16.  The
 // out-projection multiplies each row by its slot's gate weight and stores the row in fp32, so the
 // combine adds unrounded expert outputs.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
-#define FB_BM 128
-#define FB_BN 128
 #define FB_BK 64
-#define FB_LDK (FB_BK + 8)  // padded row (elements): conflict-free 16-byte LDS reads
 
 enum { MODE_IN_SWIGLU = 0, MODE_IN_RELU = 1, MODE_OUT = 2 };
 
@@ -39,24 +38,58 @@ struct FfnKArgs {
     int T, k, N, has_shared, K, Ncols, mt_max, n_tiles;
 };
 
-template <int MODE>
-__global__ __launch_bounds__(256) void ffn_bf16_kernel(FfnKArgs a) {
-    constexpr int NB = (MODE == MODE_IN_SWIGLU) ? 2 : 1;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    bf16* sA = (bf16*)smem;                 // [2][BM][LDK]
-    bf16* sB = sA + 2 * FB_BM * FB_LDK;     // [2][NB][BN][LDK]
-    __shared__ int s_info[2];
+// Tile configuration: BM rows x BNH output columns per block, WGM x WGN waves; each wave owns a
+// (BM/WGM) x (BNH/WGN) block of outputs (for SwiGLU: of both the gate and the up products).
+template <int MODE, int BM, int BNH, int WGM, int WGN>
+struct FfnTile {
+    static constexpr int NT = 64 * WGM * WGN;
+    static constexpr int NB = (MODE == MODE_IN_SWIGLU) ? 2 : 1;
+    static constexpr int BROWS = NB * BNH;           // weight rows per B tile
+    static constexpr int WTM = BM / WGM, WTN = BNH / WGN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int ROWS_PER_PASS = NT / 8;     // 8 threads x 16 B cover one 64-wide row
+    static constexpr int A_LD = BM / ROWS_PER_PASS, B_LD = BROWS / ROWS_PER_PASS;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(BM % ROWS_PER_PASS == 0 && BROWS % ROWS_PER_PASS == 0, "load passes");
+};
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    // XCD-aware order: consecutive logical tiles (the m-tiles that share one weight tile) land
-    // on the same XCD, whose L2 then serves the repeated weight reads.
-    const int G = gridDim.x;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// LDS tile layout: rows of 64 bf16 (128 B, 8 chunks of 16 B), unpadded; chunk c of row r sits at
+// position c ^ (r & 7).  The 32 lanes of a fragment read (32 consecutive rows, one chunk) then hit
+// 8 distinct 16-byte bank groups, and one wave's direct global->LDS load (64 lanes x 16 B =
+// 8 whole rows) stays contiguous: lane l writes position l & 7 of row l >> 3 and therefore
+// fetches chunk (l & 7) ^ (l >> 3) of that row.
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
+
+template <int MODE, int BM, int BNH, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
+    using Cfg = FfnTile<MODE, BM, BNH, WGM, WGN>;
+    constexpr int NB = Cfg::NB, TM = Cfg::TM, TN = Cfg::TN;
+    constexpr int NW = WGM * WGN;
+    constexpr int ROWS = BM + Cfg::BROWS;            // rows of one stage (A rows, then B rows)
+    constexpr int A_INS = BM / (8 * NW);             // load instructions per wave per stage (A)
+    constexpr int B_INS = Cfg::BROWS / (8 * NW);     // (B)
+    static_assert(BM % (8 * NW) == 0 && Cfg::BROWS % (8 * NW) == 0, "load split");
+    // two stages in two distinct LDS objects, so the compiler can tell a fragment read of one
+    // stage from the asynchronous loads into the other
+    __shared__ __attribute__((aligned(1024))) bf16 st0[ROWS * 64];
+    __shared__ __attribute__((aligned(1024))) bf16 st1[ROWS * 64];
+    __shared__ int s_info[3];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go to M0
+    // Work split.  Every block computes, from offsets, the real m-tiles of each segment
+    // (ceil(rows / BM)); the real tiles are numbered segment by segment, and within a segment
+    // n-tile by n-tile with the segment's m-tiles fastest.  The 8 XCDs get equal contiguous ranges
+    // of that numbering.  Blocks are dealt to XCDs round-robin (block b runs on XCD b % 8 as its
+    // (b / 8)-th block), so the blocks that run together on one XCD are the m-tiles of one expert
+    // against neighbouring n-tiles: they share each weight tile and their rows in that XCD's L2,
+    // and every XCD gets the same amount of real work.
     const int b = blockIdx.x;
-    const int L = (b & 7) * (G >> 3) + (b >> 3);
-    const int n_tile = L / a.mt_max, m_tile = L % a.mt_max;
-    if (n_tile >= a.n_tiles) return;
-
-    if (wave == 0) {  // segment of this m-tile: wave-wide scan of tiles per segment
+    const int xcd = b & 7, j = b >> 3;
+    if (wave == 0) {
         int tl[5], loc = 0;
 #pragma unroll
         for (int q = 0; q < 5; ++q) {
@@ -64,7 +97,7 @@ __global__ __launch_bounds__(256) void ffn_bf16_kernel(FfnKArgs a) {
             int rows = 0;
             if (s < a.N) rows = a.offsets[s + 1] - a.offsets[s];
             else if (s == a.N && a.has_shared) rows = a.T;
-            tl[q] = (rows + FB_BM - 1) / FB_BM;
+            tl[q] = (rows + BM - 1) / BM;
             loc += tl[q];
         }
         int incl = loc;
@@ -73,21 +106,28 @@ __global__ __launch_bounds__(256) void ffn_bf16_kernel(FfnKArgs a) {
             const int v = __shfl_up(incl, o, 64);
             if (lane >= o) incl += v;
         }
-        int run = incl - loc;
+        const int R = __shfl(incl, 63, 64) * a.n_tiles;
+        const int per_xcd = (R + 7) / 8;
+        const int t = (j < per_xcd) ? xcd * per_xcd + j : R;   // tile id, R = none
+        int run = (incl - loc) * a.n_tiles;
 #pragma unroll
         for (int q = 0; q < 5; ++q) {
-            if (m_tile >= run && m_tile < run + tl[q]) {
+            const int cnt = tl[q] * a.n_tiles;
+            if (t >= run && t < run + cnt) {
+                const int rem = t - run;
                 s_info[0] = lane * 5 + q;
-                s_info[1] = m_tile - run;
+                s_info[1] = rem % tl[q];
+                s_info[2] = rem / tl[q];
             }
-            run += tl[q];
+            run += cnt;
         }
-        if (lane == 63 && m_tile >= incl) s_info[0] = -1;
+        if (lane == 63 && t >= R) s_info[0] = -1;
     }
     __syncthreads();
     const int seg = s_info[0];
     if (seg < 0) return;
     const int mt = s_info[1];
+    const int n_tile = s_info[2];
     const size_t wstride = (size_t)a.Ncols * a.K;
     int row_beg, row_end;
     const bf16 *B0, *B1 = nullptr;
@@ -102,104 +142,175 @@ __global__ __launch_bounds__(256) void ffn_bf16_kernel(FfnKArgs a) {
         B0 = a.S0;
         if (NB == 2) B1 = a.S1;
     }
-    const int m0 = row_beg + mt * FB_BM;
-    const int n0 = n_tile * FB_BN;
+    const int m0 = row_beg + mt * BM;
+    const int n0 = n_tile * BNH;
 
-    // global -> register assignment: 8 threads per 64-element row, 32 rows per pass, 4 passes
-    const int kc = (tid & 7) * 8;
-    const bf16* pA[4];
-    const bf16* pB0[4];
-    const bf16* pB1[4];
+    // per-lane 32-bit byte offsets of this wave's load instructions from a uniform base
+    // (x / H stay below 4 GiB, one expert's weight matrix too)
+    const int lrow = lane >> 3;                          // row within the 8-row group
+    const int lchunk = ((lane & 7) ^ lrow) * 8;          // element offset of the fetched chunk
+    uint32_t offA[A_INS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rl = (tid >> 3) + 32 * i;
+    for (int i = 0; i < A_INS; ++i) {
+        const int rl = 8 * (wave + NW * i) + lrow;
         const int r = (m0 + rl < row_end) ? m0 + rl : m0;
         int src;
         if (MODE == MODE_OUT) src = r;
         else src = (seg < a.N) ? a.perm[r] / a.k : r - a.T * a.k;
-        pA[i] = a.A + (size_t)src * a.K + kc;
-        const int n = (n0 + rl < a.Ncols) ? n0 + rl : n0;
-        pB0[i] = B0 + (size_t)n * a.K + kc;
-        pB1[i] = (NB == 2) ? B1 + (size_t)n * a.K + kc : nullptr;
+        offA[i] = ((uint32_t)src * (uint32_t)a.K + (uint32_t)lchunk) * 2u;
     }
-    bf16x8 ra[4], rb0[4], rb1[4];
-    auto gload = [&](int k0) {
+    uint32_t offB[B_INS];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = *(const bf16x8*)(pA[i] + k0);
-            rb0[i] = *(const bf16x8*)(pB0[i] + k0);
-            if (NB == 2) rb1[i] = *(const bf16x8*)(pB1[i] + k0);
-        }
-    };
-    auto sstore = [&](int buf) {
-        bf16* dA = sA + buf * FB_BM * FB_LDK;
-        bf16* dB = sB + buf * NB * FB_BN * FB_LDK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rl = (tid >> 3) + 32 * i;
-            *(bf16x8*)(dA + rl * FB_LDK + kc) = ra[i];
-            *(bf16x8*)(dB + rl * FB_LDK + kc) = rb0[i];
-            if (NB == 2) *(bf16x8*)(dB + FB_BN * FB_LDK + rl * FB_LDK + kc) = rb1[i];
-        }
-    };
-
-    const int wm = wave >> 1, wn = wave & 1;
-    f32x16 acc[NB][2][2];
+    for (int i = 0; i < B_INS; ++i) {
+        const int br = 8 * (wave + NW * i) + lrow;       // row of the B tile
+        const int n = n0 + (br % BNH);
+        const int nc = n < a.Ncols ? n : n0;
+        offB[i] = ((uint32_t)nc * (uint32_t)a.K + (uint32_t)lchunk) * 2u;
+    }
+    const char* baseA = (const char*)a.A;
+    const char* baseB0 = (const char*)B0;
+    const char* baseB1 = (const char*)(NB == 2 ? B1 : B0);
+    const int wm = wave / WGN, wn = wave % WGN;
+    f32x16 acc[NB][TM][TN];
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    const int KT = a.K / FB_BK;
-    const int fr = lane & 31, fk = (lane >> 5) * 8;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) gload((kt + 1) * FB_BK);
-        const bf16* cA = sA + buf * FB_BM * FB_LDK + (wm * 64 + fr) * FB_LDK + fk;
-        const bf16* cB = sB + buf * NB * FB_BN * FB_LDK + (wn * 64 + fr) * FB_LDK + fk;
+    // fragment addresses: rows of one wave's fragments differ by multiples of 32, so their
+    // swizzle only depends on the lane: row r, chunk c sits at r*64 + ((c ^ (lane & 7)) << 3)
+    const int fr = lane & 31, fh = lane >> 5, l7 = lane & 7;
+    const int abase = (wm * Cfg::WTM + fr) * 64;
+    const int bbase = (BM + wn * Cfg::WTN + fr) * 64;
+    struct Frags { bf16x8 a[TM]; bf16x8 b[NB][TN]; };
+    auto load_frags = [&](const bf16* st, int kk, Frags& f) {
+        const int xo = ((2 * kk + fh) ^ l7) << 3;
 #pragma unroll
-        for (int kk = 0; kk < FB_BK; kk += 16) {
-            bf16x8 af[2], bfr[NB][2];
+        for (int i = 0; i < TM; ++i) f.a[i] = *(const bf16x8*)(st + abase + i * 32 * 64 + xo);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(cA + i * 32 * FB_LDK + kk);
+        for (int m = 0; m < NB; ++m)
 #pragma unroll
-            for (int m = 0; m < NB; ++m)
+            for (int j = 0; j < TN; ++j)
+                f.b[m][j] = *(const bf16x8*)(st + bbase + (m * BNH + j * 32) * 64 + xo);
+    };
+    // rows of this tile that exist; a tile short of BM rows (an expert's last one) skips the
+    // MFMAs of its empty 32-row sub-tiles, so it finishes early and frees its CU
+    const int rows_valid = row_end - m0;
+    const bool full_tile = rows_valid >= BM;
+    int nvi = (rows_valid - wm * Cfg::WTM + 31) / 32;
+    nvi = nvi < 0 ? 0 : (nvi > TM ? TM : nvi);
+    auto mfmas = [&](const Frags& f, auto full) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    bfr[m][j] = *(const bf16x8*)(cB + m * FB_BN * FB_LDK + j * 32 * FB_LDK + kk);
+        for (int m = 0; m < NB; ++m)
 #pragma unroll
-            for (int m = 0; m < NB; ++m)
+            for (int i = 0; i < TM; ++i) {
+                if (!decltype(full)::value && i >= nvi) continue;
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int j = 0; j < TN; ++j)
+                    acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[m][j],
+                                                                          acc[m][i][j], 0, 0, 0);
+            }
+    };
+    constexpr int NMF = NB * TM * TN;            // MFMAs per K=16 step
+    constexpr int NDS = TM + NB * TN;            // fragment reads per K=16 step
+    constexpr int NLD = A_INS + B_INS;           // direct-to-LDS loads per stage
+    constexpr int NLD0 = (NLD + 1) / 2;          // ... issued during step 0, the rest during step 1
+    // Interleave one MFMA with the step's other instructions so that a single wave per SIMD keeps
+    // the matrix core busy: MFMA, fragment read, MFMA, load, ...
+    auto interleave = [&](int n_ds, int n_ld, auto full) {
+        if (!decltype(full)::value) return;   // partial tiles: leave the order to the compiler
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[m][j],
-                                                                              acc[m][i][j], 0, 0, 0);
+        for (int i = 0; i < NMF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+            if (i < n_ds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            if (i < n_ld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
         }
-        if (kt + 1 < KT) sstore(buf ^ 1);
+    };
+    auto issue_part = [&](bf16* st, int k0, int beg, int end) {
+        const char* bA = baseA + 2 * k0;
+        const char* bB0 = baseB0 + 2 * k0;
+        const char* bB1 = baseB1 + 2 * k0;
+#pragma unroll
+        for (int q = 0; q < NLD; ++q) {
+            if (q < beg || q >= end) continue;
+            if (q < A_INS) {
+                __builtin_amdgcn_global_load_lds((gbl_void_t*)(bA + offA[q]),
+                                                 (lds_void_t*)(st + (8 * (wave + NW * q)) * 64), 16, 0, 0);
+            } else {
+                const int i = q - A_INS;
+                const int br0 = 8 * NW * i;
+                const char* bb = (NB == 2 && br0 >= BNH) ? bB1 : bB0;
+                __builtin_amdgcn_global_load_lds((gbl_void_t*)(bb + offB[i]),
+                                                 (lds_void_t*)(st + (BM + 8 * (wave + NW * i)) * 64), 16, 0, 0);
+            }
+        }
+    };
+    // One stage (K = 64 in four K=16 steps).  On entry f0 holds step 0's fragments and the
+    // first half of the next stage's loads is in flight.  The second half goes out during step 0;
+    // the barrier sits before step 3, so the next stage's first fragments are read while step 3's
+    // MFMAs run, and step 3 already sends the first half of the stage after next into the slot
+    // this stage has just released.  Loads past the last stage re-read K offset 0 into the idle
+    // slot (in bounds, never used), which keeps the schedule free of branches.
+    auto stage = [&](bf16* cur, bf16* nxt, int k_next, int k_after, Frags& f0, Frags& f1, auto full) {
+        load_frags(cur, 1, f1);
+        issue_part(nxt, k_next, NLD0, NLD);
+        mfmas(f0, full);
+        interleave(NDS, NLD - NLD0, full);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, 2, f0);
+        mfmas(f1, full);
+        interleave(NDS, 0, full);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, 3, f1);
+        mfmas(f0, full);
+        interleave(NDS, 0, full);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0070);    // vmcnt(0) lgkmcnt(0): own loads and reads done
+        __syncthreads();                       // next stage visible; this stage no longer read
+        load_frags(nxt, 0, f0);
+        issue_part(cur, k_after, 0, NLD0);
+        mfmas(f1, full);
+        interleave(NDS, NLD0, full);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    const int KT = a.K / FB_BK;
+    auto kofs = [&](int t) { return (t < KT ? t : 0) * FB_BK; };
+    auto run = [&](auto full) {
+        Frags fa, fb;
+        issue_part(st0, 0, 0, NLD);
+        __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
-    }
+        load_frags(st0, 0, fa);
+        issue_part(st1, kofs(1), 0, NLD0);
+        int kt = 0;
+        for (; kt + 2 <= KT; kt += 2) {
+            stage(st0, st1, kofs(kt + 1), kofs(kt + 2), fa, fb, full);
+            stage(st1, st0, kofs(kt + 2), kofs(kt + 3), fa, fb, full);
+        }
+        if (kt < KT) stage(st0, st1, 0, 0, fa, fb, full);
+        __builtin_amdgcn_s_waitcnt(0x0070);    // no load may still be writing LDS at exit
+    };
+    if (full_tile) run(std::true_type{});
+    else run(std::false_type{});
 
     // epilogue.  32x32 C layout: lane holds column (lane & 31); register r holds row
     // 8*(r >> 2) + 4*(lane >> 5) + (r & 3).
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int row = m0 + wm * Cfg::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if (row >= row_end) continue;
             float scale = 1.0f;
             if (MODE == MODE_OUT && a.row_scale && seg < a.N) scale = a.row_scale[a.perm[row]];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+            for (int j = 0; j < TN; ++j) {
+                const int col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
                 if (col >= a.Ncols) continue;
                 float v;
                 if (MODE == MODE_IN_SWIGLU) v = silu_f32(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
@@ -266,32 +377,21 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------------ launchers
-static size_t ffn_smem_bytes(int mode) {
-    const int nb = (mode == MODE_IN_SWIGLU) ? 2 : 1;
-    return (size_t)(2 * FB_BM * FB_LDK + 2 * nb * FB_BN * FB_LDK) * sizeof(bf16);
+template <int MODE, int BM, int BNH, int WGM, int WGN>
+static hipError_t launch_bf16(const FfnKArgs& ka, hipStream_t s) {
+    using Cfg = FfnTile<MODE, BM, BNH, WGM, WGN>;
+    auto kern = ffn_bf16_kernel<MODE, BM, BNH, WGM, WGN>;
+    FfnKArgs a = ka;
+    a.mt_max = (a.T * a.k + BM - 1) / BM + a.N + (a.has_shared ? (a.T + BM - 1) / BM : 0);
+    a.n_tiles = (a.Ncols + BNH - 1) / BNH;
+    const long long G = 8 * (((long long)a.mt_max * a.n_tiles + 7) / 8);
+    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), 0, s, a);
+    return hipGetLastError();
 }
 
-template <int MODE>
-static hipError_t launch_bf16(const FfnKArgs& ka, int T, int k, int N, int has_shared, hipStream_t s) {
-    // the LDS limit above 64 KiB is a per-function, per-device attribute; set it once per device
-    static bool attr_set[64] = {};
-    const size_t smem = ffn_smem_bytes(MODE);
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-        e = hipFuncSetAttribute((const void*)ffn_bf16_kernel<MODE>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) attr_set[dev] = true;
-    }
-    FfnKArgs a = ka;
-    a.mt_max = (T * k + FB_BM - 1) / FB_BM + N + (has_shared ? (T + FB_BM - 1) / FB_BM : 0);
-    a.n_tiles = (a.Ncols + FB_BN - 1) / FB_BN;
-    long long G = (long long)a.mt_max * a.n_tiles;
-    G = (G + 7) / 8 * 8;
-    hipLaunchKernelGGL(ffn_bf16_kernel<MODE>, dim3((unsigned)G), dim3(256), smem, s, a);
-    return hipGetLastError();
+// Tile choice from what the host knows (T, k, N, widths): rows per expert on average.
+static bool big_tiles(const FfnLaunch& f) {
+    return (long long)f.T * f.k >= 512LL * f.N;   // >= 512 rows per expert on average
 }
 
 hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
@@ -308,11 +408,13 @@ hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
         if (f.ffn == 1) {
             a.B0 = (const bf16*)f.w_gate; a.B1 = (const bf16*)f.w_up;
             a.S0 = (const bf16*)f.sh_gate; a.S1 = (const bf16*)f.sh_up;
-            return launch_bf16<MODE_IN_SWIGLU>(a, f.T, f.k, f.N, f.has_shared, s);
+            if (big_tiles(f)) return launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, s);
+            return launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, s);
         }
         a.B0 = (const bf16*)f.w_up;
         a.S0 = (const bf16*)f.sh_up;
-        return launch_bf16<MODE_IN_RELU>(a, f.T, f.k, f.N, f.has_shared, s);
+        if (big_tiles(f)) return launch_bf16<MODE_IN_RELU, 256, 256, 2, 2>(a, s);
+        return launch_bf16<MODE_IN_RELU, 128, 128, 2, 2>(a, s);
     }
     const long long n = rows_total * f.d_ff;
     const dim3 grid((unsigned)((n + 255) / 256));
@@ -340,7 +442,8 @@ hipError_t launch_ffn_out(const FfnLaunch& f, hipStream_t s) {
         a.C = f.y_perm;
         a.T = f.T; a.k = f.k; a.N = f.N; a.has_shared = f.has_shared;
         a.K = f.d_ff; a.Ncols = f.d;
-        return launch_bf16<MODE_OUT>(a, f.T, f.k, f.N, f.has_shared, s);
+        if (big_tiles(f)) return launch_bf16<MODE_OUT, 256, 256, 2, 2>(a, s);
+        return launch_bf16<MODE_OUT, 128, 128, 2, 2>(a, s);
     }
     const long long rows_total = (long long)f.T * f.k + (f.has_shared ? f.T : 0);
     const long long n = rows_total * f.d;

@@ -66,7 +66,9 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
-__device__ __forceinline__ float silu_f32(float u) { return u / (1.0f + __expf(-u)); }
+// silu(u) = u * sigmoid(u) = u / (1 + e^-u), with the hardware reciprocal (about 1 ulp); for
+// u -> -inf the reciprocal of +inf is 0 and the result -0.
+__device__ __forceinline__ float silu_f32(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
 
 // Host-side launch status helper.
 struct LaunchCheck {

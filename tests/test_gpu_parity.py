@@ -50,6 +50,11 @@ SMALL = {
                                ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=12),
     "relu_shared_modeb": W.LayerConfig("relu_shared_modeb", T=130, d=64, N=16, k=4, d_ff=128, dtype="bf16",
                                        ffn=W.FFN_RELU2, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=13),
+    # >= 512 rows per expert: the large-tile GEMM configuration, with partial n-tiles
+    "big_tiles_swiglu": W.LayerConfig("big_tiles_swiglu", T=700, d=128, N=2, k=2, d_ff=384, dtype="bf16",
+                                      ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=15),
+    "big_tiles_relu": W.LayerConfig("big_tiles_relu", T=600, d=320, N=2, k=2, d_ff=320, dtype="bf16",
+                                    ffn=W.FFN_RELU2, gating=W.GATE_TOPK_SOFTMAX, seed=16),
 }
 
 
