@@ -82,6 +82,93 @@ def algorithmic_counts(cfg, counts):
                 ffn_in_flops=ffn_in_flops, ffn_in_bytes=ffn_in_bytes)
 
 
+FFN_SOURCE = os.path.join(ROOT, "mixture_experts_layer_48_amd", "csrc", "ffn.hip")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """Short hash of the grouped-GEMM source: counter figures are only reused while it is unchanged."""
+    import hashlib
+    with open(FFN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch of the in-projection kernel from the committed counter summary
+    (profiles/ffn_in_<workload>_traffic.txt), or None if there is none or the kernel source
+    changed since the counters were taken."""
+    path = os.path.join(TRAFFIC_DIR, f"ffn_in_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for ln in f:
+            if "=" in ln and not ln.startswith("#"):
+                k, v = ln.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str, command: str) -> str:
+    """Text summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch):
+    each counter is scaled by what it reads for a plain copy of copy_bytes."""
+    import csv
+    import glob
+    import statistics
+
+    def per_kernel(d, counter):
+        out = {}
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(fn)):
+                if r["Counter_Name"] == counter:
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        ks = [k for k in d if key in k]
+        return statistics.mean(d[ks[0]]) if ks else float("nan")
+
+    def largest(d, key):
+        # the calibration copy is by far the largest copy dispatch of the run
+        vals = [v for k, vs in d.items() if key in k for v in vs]
+        return max(vals) if vals else float("nan")
+
+    copy_f, copy_w = largest(fetch, "copy"), largest(write, "copy")
+    f_scale = copy_bytes / (copy_f * 1024.0)
+    w_scale = copy_bytes / (copy_w * 1024.0)
+    ffn_f, ffn_w = pick(fetch, "ffn_bf16_kernel<0"), pick(write, "ffn_bf16_kernel<0")
+    hbm = ffn_f * 1024.0 * f_scale + ffn_w * 1024.0 * w_scale
+    lines = [
+        f"# HBM traffic of the grouped gate/up projection kernel (ffn_bf16_kernel<0,...>), {workload}",
+        f"# command: {command}",
+        "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by bytes/KiB it reads",
+        f"# for a plain device copy of {copy_bytes} bytes in the same run.",
+        f"workload = {workload}",
+        f"copy_bytes = {copy_bytes}",
+        f"copy_fetch_kib = {copy_f:.1f}",
+        f"copy_write_kib = {copy_w:.1f}",
+        f"fetch_scale = {f_scale:.4f}",
+        f"write_scale = {w_scale:.4f}",
+        f"ffn_in_fetch_kib_per_dispatch = {ffn_f:.1f}",
+        f"ffn_in_write_kib_per_dispatch = {ffn_w:.1f}",
+        f"hbm_bytes_per_launch = {hbm:.0f}",
+        f"kernel_source_sha256_16 = {kernel_source_hash()}",
+    ]
+    for name, vals in sorted(fetch.items()):
+        lines.append(f"# fetch_kib {statistics.mean(vals):14.1f}  {name[:90]}")
+    for name, vals in sorted(write.items()):
+        lines.append(f"# write_kib {statistics.mean(vals):14.1f}  {name[:90]}")
+    return "\n".join(lines) + "\n"
+
+
 def cpu_baseline(cfg, inp, sample_tokens: int):
     """The float64 CPU oracle, as it stands, on the first `sample_tokens` tokens of the same layer
     (same weights; the oracle reads each touched expert's weights once, converted to float64)."""
@@ -126,7 +213,15 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default="mixtral_prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB", "COMMAND"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        fd, wd, mib, cmd = args.summarize_pmc
+        sys.stdout.write(summarize_pmc(fd, wd, int(mib) << 20, args.config, cmd))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU's share of the layer; --gpus {args.gpus} is not "
               f"supported (run with --gpus 1)", file=sys.stderr)
@@ -142,6 +237,14 @@ def main(argv=None) -> int:
         return 1
     cfg = W.CONFIGS[args.config]
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     inp = W.make_inputs(cfg, "cuda")
     desc = M.make_desc(cfg.T, cfg.d, cfg.N, cfg.k, cfg.d_ff, cfg.dtype, cfg.ffn, cfg.gating,
                        cfg.capacity_factor, cfg.has_shared)
@@ -184,7 +287,7 @@ def main(argv=None) -> int:
         roof = {"bound": "hbm", "achieved": alg["ffn_in_bytes"] / (ffn_in_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = traffic_from_profile(cfg.name)
     roof["kernel"] = "ffn_in (grouped gate/up projection)"
     out = {
         "metric": METRIC,
@@ -212,8 +315,9 @@ def main(argv=None) -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        default_sample = {"tiny_fp32": 128, "mixtral_prefill": 256, "mixtral_decode": 16,
-                          "deepseek_v3": 64, "skewed_capacity": 512}.get(cfg.name, 64)
+        # samples sized for roughly 10-30 s of oracle work on a 16-core host
+        default_sample = {"tiny_fp32": 128, "mixtral_prefill": 1024, "mixtral_decode": 16,
+                          "deepseek_v3": 256, "skewed_capacity": 2048}.get(cfg.name, 64)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens or default_sample)
     print(json.dumps(out), flush=True)
     return 0

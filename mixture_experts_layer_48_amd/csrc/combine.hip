@@ -8,37 +8,48 @@
 #include "moe_common.h"
 #include "moe_kernels.h"
 
+// A row's value is the sum of its nparts K-part partials (added in part order), then
+// weighted; part p of row r sits at yp + p * part_stride + r * d.
+__device__ __forceinline__ void row8(const float* __restrict__ yp, long long part_stride, int nparts,
+                                     size_t off, float v[8]) {
+    f32x4 a = *(const f32x4*)(yp + off), b = *(const f32x4*)(yp + off + 4);
+    for (int p = 1; p < nparts; ++p) {
+        const f32x4 c = *(const f32x4*)(yp + p * part_stride + off);
+        const f32x4 e = *(const f32x4*)(yp + p * part_stride + off + 4);
+        a += c;
+        b += e;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = a[i];
+        v[i + 4] = b[i];
+    }
+}
+
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const float* __restrict__ yp,
                                                            const int32_t* __restrict__ inv,
                                                            const float* __restrict__ w,
                                                            bf16* __restrict__ y, int T, int k, int d,
-                                                           int has_shared) {
+                                                           int has_shared, int nparts) {
     const int t = blockIdx.x;
     const int32_t* iv = inv + (size_t)t * k;
     const float* wv = w ? w + (size_t)t * k : nullptr;
-    const float* ysh = yp + ((size_t)T * k + t) * d;
+    const long long part_stride = ((long long)T * k + (has_shared ? T : 0)) * d;
     for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float v[8];
         for (int j = 0; j < k; ++j) {
             const int r = iv[j];
             if (r < 0) continue;
             const float s = wv ? wv[j] : 1.0f;
-            const f32x4 v0 = *(const f32x4*)(yp + (size_t)r * d + c);
-            const f32x4 v1 = *(const f32x4*)(yp + (size_t)r * d + c + 4);
+            row8(yp, part_stride, nparts, (size_t)r * d + c, v);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[i] = fmaf(s, v0[i], acc[i]);
-                acc[i + 4] = fmaf(s, v1[i], acc[i + 4]);
-            }
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(s, v[i], acc[i]);
         }
         if (has_shared) {
-            const f32x4 v0 = *(const f32x4*)(ysh + c);
-            const f32x4 v1 = *(const f32x4*)(ysh + c + 4);
+            row8(yp, part_stride, nparts, ((size_t)T * k + t) * d + c, v);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[i] += v0[i];
-                acc[i + 4] += v1[i];
-            }
+            for (int i = 0; i < 8; ++i) acc[i] += v[i];
         }
         bf16x8 o;
 #pragma unroll
@@ -68,11 +79,11 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
 }
 
 hipError_t launch_combine(const void* y_perm, const int32_t* inv, const float* w, void* y, int T,
-                          int k, int d, int has_shared, int dtype, hipStream_t s) {
+                          int k, int d, int has_shared, int dtype, int nparts, hipStream_t s) {
     if (T == 0) return hipSuccess;
     if (dtype == 1)
         hipLaunchKernelGGL(combine_bf16_kernel, dim3(T), dim3(256), 0, s, (const float*)y_perm, inv, w,
-                           (bf16*)y, T, k, d, has_shared);
+                           (bf16*)y, T, k, d, has_shared, nparts < 1 ? 1 : nparts);
     else
         hipLaunchKernelGGL(combine_f32_kernel, dim3(T), dim3(256), 0, s, (const float*)y_perm, inv, w,
                            (float*)y, T, k, d, has_shared);

@@ -36,6 +36,8 @@ struct FfnKArgs {
     const float* row_scale; // [T*k] or null (out-projection only)
     void* C;                // [rows, Ncols]: bf16 H (in-projection) or fp32 y_perm (out-projection)
     int T, k, N, has_shared, K, Ncols, mt_max, n_tiles;
+    int ksplit;             // K is split into ksplit equal parts (out-projection only)
+    long long part_stride;  // elements between the fp32 partial outputs of the K parts
 };
 
 // Tile configuration: BM rows x BNH output columns per block, WGM x WGN waves; each wave owns a
@@ -57,11 +59,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 // LDS tile layout: rows of 64 bf16 (128 B, 8 chunks of 16 B), unpadded; chunk c of row r sits at
-// position c ^ (r & 7).  The 32 lanes of a fragment read (32 consecutive rows, one chunk) then hit
-// 8 distinct 16-byte bank groups, and one wave's direct global->LDS load (64 lanes x 16 B =
-// 8 whole rows) stays contiguous: lane l writes position l & 7 of row l >> 3 and therefore
-// fetches chunk (l & 7) ^ (l >> 3) of that row.
-__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
+// position c ^ ((r >> 1) & 7).  A fragment read serves 16 lanes (16 consecutive rows, one chunk,
+// 256 B) per LDS cycle; with this swizzle those 16 reads land in 16 distinct 16-byte bank groups
+// of the 64 banks.  One wave's direct global->LDS load (64 lanes x 16 B = 8 whole rows) stays
+// contiguous in LDS: lane l writes position l & 7 of row 8g + (l >> 3) and therefore fetches
+// chunk (l & 7) ^ ((4g + (l >> 4)) & 7) of that row.
 
 template <int MODE, int BM, int BNH, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     // stage from the asynchronous loads into the other
     __shared__ __attribute__((aligned(1024))) bf16 st0[ROWS * 64];
     __shared__ __attribute__((aligned(1024))) bf16 st1[ROWS * 64];
-    __shared__ int s_info[3];
+    __shared__ int s_info[4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go to M0
@@ -106,9 +108,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
             const int v = __shfl_up(incl, o, 64);
             if (lane >= o) incl += v;
         }
-        const int R = __shfl(incl, 63, 64) * a.n_tiles;
+        const int R1 = __shfl(incl, 63, 64) * a.n_tiles;   // tiles of one K part
+        const int R = R1 * a.ksplit;
         const int per_xcd = (R + 7) / 8;
-        const int t = (j < per_xcd) ? xcd * per_xcd + j : R;   // tile id, R = none
+        int t = (j < per_xcd) ? xcd * per_xcd + j : R;     // tile id, R = none
+        const int ks = t < R ? t / R1 : 0;                  // K part (outermost)
+        if (t < R) t -= ks * R1;
+        else t = R1;
         int run = (incl - loc) * a.n_tiles;
 #pragma unroll
         for (int q = 0; q < 5; ++q) {
@@ -121,13 +127,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
             }
             run += cnt;
         }
-        if (lane == 63 && t >= R) s_info[0] = -1;
+        if (lane == 63 && t >= R1) s_info[0] = -1;
+        if (lane == 0) s_info[3] = ks;
     }
     __syncthreads();
     const int seg = s_info[0];
     if (seg < 0) return;
     const int mt = s_info[1];
     const int n_tile = s_info[2];
+    const int kpart = s_info[3];
     const size_t wstride = (size_t)a.Ncols * a.K;
     int row_beg, row_end;
     const bf16 *B0, *B1 = nullptr;
@@ -148,7 +156,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     // per-lane 32-bit byte offsets of this wave's load instructions from a uniform base
     // (x / H stay below 4 GiB, one expert's weight matrix too)
     const int lrow = lane >> 3;                          // row within the 8-row group
-    const int lchunk = ((lane & 7) ^ lrow) * 8;          // element offset of the fetched chunk
+    // element offset of the chunk lane fetches for LDS row group g (8 rows)
+    auto lchunk = [&](int g) { return ((lane & 7) ^ ((4 * g + (lane >> 4)) & 7)) * 8; };
     uint32_t offA[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         int src;
         if (MODE == MODE_OUT) src = r;
         else src = (seg < a.N) ? a.perm[r] / a.k : r - a.T * a.k;
-        offA[i] = ((uint32_t)src * (uint32_t)a.K + (uint32_t)lchunk) * 2u;
+        offA[i] = ((uint32_t)src * (uint32_t)a.K + (uint32_t)lchunk(wave + NW * i)) * 2u;
     }
     uint32_t offB[B_INS];
 #pragma unroll
@@ -165,7 +174,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         const int br = 8 * (wave + NW * i) + lrow;       // row of the B tile
         const int n = n0 + (br % BNH);
         const int nc = n < a.Ncols ? n : n0;
-        offB[i] = ((uint32_t)nc * (uint32_t)a.K + (uint32_t)lchunk) * 2u;
+        offB[i] = ((uint32_t)nc * (uint32_t)a.K + (uint32_t)lchunk((BM >> 3) + wave + NW * i)) * 2u;
     }
     const char* baseA = (const char*)a.A;
     const char* baseB0 = (const char*)B0;
@@ -182,8 +191,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
                 for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
 
     // fragment addresses: rows of one wave's fragments differ by multiples of 32, so their
-    // swizzle only depends on the lane: row r, chunk c sits at r*64 + ((c ^ (lane & 7)) << 3)
-    const int fr = lane & 31, fh = lane >> 5, l7 = lane & 7;
+    // swizzle only depends on the lane: row r, chunk c sits at r*64 + ((c ^ ((r >> 1) & 7)) << 3)
+    const int fr = lane & 31, fh = lane >> 5, l7 = (fr >> 1) & 7;
     const int abase = (wm * Cfg::WTM + fr) * 64;
     const int bbase = (BM + wn * Cfg::WTN + fr) * 64;
     struct Frags { bf16x8 a[TM]; bf16x8 b[NB][TN]; };
@@ -278,11 +287,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    const int KT = a.K / FB_BK;
-    auto kofs = [&](int t) { return (t < KT ? t : 0) * FB_BK; };
+    const int KT = a.K / FB_BK / a.ksplit;                 // stages of this K part
+    const int kbase = kpart * KT * FB_BK;
+    auto kofs = [&](int t) { return kbase + (t < KT ? t : 0) * FB_BK; };
     auto run = [&](auto full) {
         Frags fa, fb;
-        issue_part(st0, 0, 0, NLD);
+        issue_part(st0, kbase, 0, NLD);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
         load_frags(st0, 0, fa);
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
             stage(st0, st1, kofs(kt + 1), kofs(kt + 2), fa, fb, full);
             stage(st1, st0, kofs(kt + 2), kofs(kt + 3), fa, fb, full);
         }
-        if (kt < KT) stage(st0, st1, 0, 0, fa, fb, full);
+        if (kt < KT) stage(st0, st1, kbase, kbase, fa, fb, full);
         __builtin_amdgcn_s_waitcnt(0x0070);    // no load may still be writing LDS at exit
     };
     if (full_tile) run(std::true_type{});
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
                 if (MODE == MODE_IN_SWIGLU) v = silu_f32(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
                 else if (MODE == MODE_IN_RELU) v = fmaxf(acc[0][i][j][r], 0.f);
                 else v = acc[0][i][j][r] * scale;
-                if (MODE == MODE_OUT) ((float*)a.C)[(size_t)row * a.Ncols + col] = v;
+                if (MODE == MODE_OUT) ((float*)a.C)[kpart * a.part_stride + (size_t)row * a.Ncols + col] = v;
                 else ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)v;
             }
         }
@@ -382,16 +392,28 @@ static hipError_t launch_bf16(const FfnKArgs& ka, hipStream_t s) {
     using Cfg = FfnTile<MODE, BM, BNH, WGM, WGN>;
     auto kern = ffn_bf16_kernel<MODE, BM, BNH, WGM, WGN>;
     FfnKArgs a = ka;
+    if (a.ksplit < 1) a.ksplit = 1;
     a.mt_max = (a.T * a.k + BM - 1) / BM + a.N + (a.has_shared ? (a.T + BM - 1) / BM : 0);
     a.n_tiles = (a.Ncols + BNH - 1) / BNH;
-    const long long G = 8 * (((long long)a.mt_max * a.n_tiles + 7) / 8);
+    const long long G = 8 * (((long long)a.mt_max * a.n_tiles * a.ksplit + 7) / 8);
     hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), 0, s, a);
     return hipGetLastError();
 }
 
 // Tile choice from what the host knows (T, k, N, widths): rows per expert on average.
 static bool big_tiles(const FfnLaunch& f) {
-    return (long long)f.T * f.k >= 512LL * f.N;   // >= 512 rows per expert on average
+    return (long long)f.T * f.k >= 192LL * f.N;   // >= 192 rows per expert on average
+}
+
+// K parts for the out-projection: two when its K is long and one part alone would leave the
+// last round of blocks on the CUs mostly empty.  The parts' fp32 outputs are summed, in order,
+// by the combine.
+int ffn_out_ksplit(int T, int k, int N, int d, int d_ff, int has_shared, int dtype) {
+    if (dtype != 1 || d_ff % (2 * FB_BK) != 0 || d_ff < 8192) return 1;
+    const long long rows = (long long)T * k;
+    if (rows < 192LL * N) return 1;                       // small-tile path: many blocks already
+    const long long tiles = ((rows + 255) / 256 + N + (has_shared ? (T + 255) / 256 : 0)) * ((d + 255) / 256);
+    return tiles < 4 * 256 ? 2 : 1;
 }
 
 hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
@@ -442,6 +464,8 @@ hipError_t launch_ffn_out(const FfnLaunch& f, hipStream_t s) {
         a.C = f.y_perm;
         a.T = f.T; a.k = f.k; a.N = f.N; a.has_shared = f.has_shared;
         a.K = f.d_ff; a.Ncols = f.d;
+        a.ksplit = f.ksplit;
+        a.part_stride = (long long)((long long)f.T * f.k + (f.has_shared ? f.T : 0)) * f.d;
         if (big_tiles(f)) return launch_bf16<MODE_OUT, 256, 256, 2, 2>(a, s);
         return launch_bf16<MODE_OUT, 128, 128, 2, 2>(a, s);
     }

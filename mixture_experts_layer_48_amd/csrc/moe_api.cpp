@@ -75,6 +75,10 @@ moe_status check_weights(const moe_layer_desc& d, const moe_weights* w, bool nee
     return MOE_OK;
 }
 
+int ksplit_of(const moe_layer_desc& d) {
+    return ffn_out_ksplit(d.T, d.k, d.N, d.d, d.d_ff, d.has_shared, d.dtype);
+}
+
 // Workspace of the whole forward, carved in this order (each piece 256-byte aligned).
 struct Layout {
     size_t z, ranked, idx, w, counts, offsets, perm, inv, h, yp, total;
@@ -92,7 +96,8 @@ Layout layout_of(const moe_layer_desc& d) {
     L.perm = o; o += align256(T * k * 4);
     L.inv = o; o += align256(T * k * 4);
     L.h = o; o += align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d));
-    L.yp = o; o += align256((size_t)rows_total(d) * d.d * 4);  // fp32 expert rows
+    // fp32 expert rows, one copy per K part of the out-projection
+    L.yp = o; o += align256((size_t)rows_total(d) * d.d * 4 * ksplit_of(d));
     L.total = o;
     return L;
 }
@@ -135,6 +140,7 @@ FfnLaunch ffn_args(const moe_layer_desc& d, const moe_weights& wt, const void* x
     f.w_gate = wt.w_gate; f.w_up = wt.w_up; f.w_down = wt.w_down;
     f.sh_gate = wt.sh_gate; f.sh_up = wt.sh_up; f.sh_down = wt.sh_down;
     f.row_scale = row_scale; f.h = h; f.y_perm = yp;
+    f.ksplit = 1;
     return f;
 }
 
@@ -223,7 +229,7 @@ moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int
     const moe_layer_desc& d = *desc;
     if (d.T == 0) return MOE_OK;
     if (!y_perm || !inv || !y) return fail(MOE_ERR_INVALID_ARG, "y_perm, inv and y are required");
-    hipError_t e = launch_combine(y_perm, inv, w, y, d.T, d.k, d.d, d.has_shared, d.dtype, (hipStream_t)stream);
+    hipError_t e = launch_combine(y_perm, inv, w, y, d.T, d.k, d.d, d.has_shared, d.dtype, 1, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 
@@ -266,13 +272,14 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_weights
     if (e != hipSuccess) return hip_fail(e, "permute launch");
     if ((st = record(ev(3), s)) != MOE_OK) return st;
     FfnLaunch f = ffn_args(d, *weights, x, perm, offsets, w, h, yp);
+    f.ksplit = ksplit_of(d);
     e = launch_ffn_in(f, s);
     if (e != hipSuccess) return hip_fail(e, "ffn in-projection launch");
     if ((st = record(ev(4), s)) != MOE_OK) return st;
     e = launch_ffn_out(f, s);
     if (e != hipSuccess) return hip_fail(e, "ffn out-projection launch");
     if ((st = record(ev(5), s)) != MOE_OK) return st;
-    e = launch_combine(yp, inv, nullptr, y, d.T, d.k, d.d, d.has_shared, d.dtype, s);
+    e = launch_combine(yp, inv, nullptr, y, d.T, d.k, d.d, d.has_shared, d.dtype, f.ksplit, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return record(ev(6), s);
 }

@@ -30,9 +30,11 @@ struct FfnLaunch {
     const void* sh_down;
     const float* row_scale;   // [T*k] or null
     void* h;                  // [T*k + T, d_ff] hidden state
-    void* y_perm;             // [T*k + T, d]
+    void* y_perm;             // [ksplit][T*k + T, d] fp32 (ksplit partial sums)
+    int ksplit;               // K parts of the out-projection (1 = y_perm holds the result)
 };
+int ffn_out_ksplit(int T, int k, int N, int d, int d_ff, int has_shared, int dtype);
 hipError_t launch_ffn_in(const FfnLaunch& a, hipStream_t s);   // H = act(x W_in)
 hipError_t launch_ffn_out(const FfnLaunch& a, hipStream_t s);  // y_perm = scale * H W_out
 hipError_t launch_combine(const void* y_perm, const int32_t* inv, const float* w, void* y, int T,
-                          int k, int d, int has_shared, int dtype, hipStream_t s);
+                          int k, int d, int has_shared, int dtype, int nparts, hipStream_t s);

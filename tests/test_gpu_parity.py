@@ -55,6 +55,9 @@ SMALL = {
                                       ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=15),
     "big_tiles_relu": W.LayerConfig("big_tiles_relu", T=600, d=320, N=2, k=2, d_ff=320, dtype="bf16",
                                     ffn=W.FFN_RELU2, gating=W.GATE_TOPK_SOFTMAX, seed=16),
+    # long out-projection K: the down projection runs as two K parts summed by the combine
+    "split_k_out": W.LayerConfig("split_k_out", T=200, d=128, N=2, k=2, d_ff=8192, dtype="bf16",
+                                 ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=17),
 }
 
 
