@@ -88,7 +88,7 @@ Layout layout_of(const moe_layer_desc& d) {
     size_t o = 0;
     const size_t T = (size_t)d.T, N = (size_t)d.N, k = (size_t)d.k;
     L.z = o; o += align256(T * N * 4);
-    L.ranked = o; o += has_capacity(d) ? align256(T * N) : 0;
+    L.ranked = o; o += has_capacity(d) ? align256(capacity_workspace_bytes(d.T, d.N)) : 0;
     L.idx = o; o += align256(T * k * 4);
     L.w = o; o += align256(T * k * 4);
     L.counts = o; o += align256(N * 4);
@@ -103,7 +103,7 @@ Layout layout_of(const moe_layer_desc& d) {
 }
 size_t route_ws_bytes(const moe_layer_desc& d, bool have_logits) {
     return (have_logits ? 0 : align256((size_t)d.T * d.N * 4)) +
-           (has_capacity(d) ? align256((size_t)d.T * d.N) : 0);
+           (has_capacity(d) ? align256(capacity_workspace_bytes(d.T, d.N)) : 0);
 }
 size_t ffn_ws_bytes(const moe_layer_desc& d) {
     return align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d));

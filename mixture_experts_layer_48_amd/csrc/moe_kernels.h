@@ -8,6 +8,9 @@ hipError_t launch_router_logits(const void* x, const void* wr, const float* bias
                                 int d, int N, int dtype, hipStream_t s);
 hipError_t launch_topk_gate(const float* z, int T, int N, int k, int gating, int32_t* idx, float* w,
                             hipStream_t s);
+// workspace of the capacity step: ranked lists [T, capacity_ranked_stride(N)] bytes, then [T]
+int capacity_ranked_stride(int N);
+size_t capacity_workspace_bytes(int T, int N);
 hipError_t launch_capacity(const float* z, uint8_t* ranked, int T, int N, int k, int C, int gating,
                            int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int N, int32_t* counts, int32_t* offsets,

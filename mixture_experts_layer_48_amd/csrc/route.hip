@@ -172,8 +172,9 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(
 
 // ------------------------------------------------------------------ full ranking (capacity)
 // One token per 64-thread block: bitonic sort of the N ranking keys in LDS, descending.
-// ranked[t, r] = expert of rank r (uint8, N <= 256).
-__global__ __launch_bounds__(64) void rank_sort_kernel(const float* __restrict__ z, int T, int N,
+// ranked[t * NP + r] = expert of rank r (uint8, N <= 256); rows are padded to NP = N rounded up
+// to 16 bytes with 0xFF, which is never a valid expert when padding exists (N < 256).
+__global__ __launch_bounds__(64) void rank_sort_kernel(const float* __restrict__ z, int T, int N, int NP,
                                                        uint8_t* __restrict__ ranked) {
     __shared__ uint64_t key[MOE_MAX_EXPERTS];
     const int t = blockIdx.x, lane = threadIdx.x;
@@ -194,120 +195,207 @@ __global__ __launch_bounds__(64) void rank_sort_kernel(const float* __restrict__
             __syncthreads();
         }
     }
-    for (int r = lane; r < N; r += 64) ranked[(size_t)t * N + r] = (uint8_t)key_expert(key[r]);
+    for (int r = lane; r < NP; r += 64)
+        ranked[(size_t)t * NP + r] = r < N ? (uint8_t)key_expert(key[r]) : (uint8_t)0xFF;
 }
 
 // ------------------------------------------------------------------ capacity routing
 // One block of 1024 threads.  Slots are placed pass by pass (all slot-0s in token order, then
-// all slot-1s, ...).  Within a pass, tokens are taken in chunks of 1024 (one per thread); the
-// chunk is resolved in parallel by deferred acceptance with token order as every expert's
-// priority: each token proposes to its best expert that it does not hold, that had room at the
-// start of the chunk and whose current cut-off tau[e] is not below the token; an expert keeps
-// its (room)-th first proposers in token order and moves tau[e] to the last one kept.  tau only
-// moves down, so a token never returns to an expert that turned it away, and the fixed point
-// is the token-by-token first-come assignment.
+// all slot-1s, ...).  Within a pass, tokens are taken in chunks of CT (one per thread); a chunk
+// is resolved in parallel by deferred acceptance with token order as every expert's priority:
+// each token proposes to its best-ranked expert that it does not hold, that had room at the
+// start of the chunk and whose cut-off tau[e] is not below the token; an expert keeps its
+// (room)-th first proposers in token order and moves tau[e] to the last one kept.  tau only moves
+// down, so a token never returns to an expert that turned it away, and the fixed point is the
+// token-by-token first-come assignment.
+//
+// The chunk's ranked lists sit in LDS (4 ranks per dword, rank-major, so a wave's lanes read
+// neighbouring words); "room at chunk start" and "already held" are bits in registers, so a
+// token steps over full experts without touching memory.  Proposal counts are per wave, stamped
+// with the round number, so no round has to clear them.
 #define CAP_THREADS 1024
 #define CAP_WAVES (CAP_THREADS / 64)
+#define CAP_RK_WORDS 24576          // 96 KiB of ranked lists per chunk
 
-__global__ __launch_bounds__(CAP_THREADS) void capacity_kernel(
-    const uint8_t* __restrict__ ranked, const float* __restrict__ z, int T, int N, int k, int C,
-    int gating, int32_t* __restrict__ idx, float* __restrict__ w) {
+// NVMAX: 16-byte pieces of a ranked row kept in registers (8: N <= 128, 16: N <= 256); THREADS:
+// block size (1024, or 512 so that the 16 pieces fit the register budget).
+template <int NVMAX, int THREADS>
+__global__ __launch_bounds__(THREADS) void capacity_kernel(
+    const uint8_t* __restrict__ ranked, uint8_t* __restrict__ rpos, int T, int N, int NP, int CT, int k,
+    int C, int32_t* __restrict__ idx) {
+    constexpr int CAP_THREADS_ = THREADS;
+    constexpr int CAP_WAVES_ = THREADS / 64;
+    __shared__ uint32_t rk4[CAP_RK_WORDS];              // [NP / 4][CT]
+    __shared__ uint32_t cnt[CAP_WAVES_][MOE_MAX_EXPERTS]; // (round << 16) | proposals of the wave
     __shared__ int fill[MOE_MAX_EXPERTS];
     __shared__ int tau[MOE_MAX_EXPERTS];
-    __shared__ int wcnt[CAP_WAVES][MOE_MAX_EXPERTS];
-    __shared__ uint32_t held[MOE_MAX_EXPERTS / 32][CAP_THREADS];  // experts the token already holds
-    const int tid = threadIdx.x, wave = tid >> 6;
-    for (int e = tid; e < N; e += CAP_THREADS) fill[e] = 0;
+    __shared__ uint8_t roomb[MOE_MAX_EXPERTS];          // 1: expert had room at chunk start
+    const int tid = threadIdx.x, lane = tid & 63;
+    (void)lane;
+    const int wave = tid >> 6;
+    const int NQ = NP >> 2;               // words per ranked row (multiple of 4)
+    const int NV = NQ >> 2;               // 16-byte pieces per ranked row (<= 16)
+    for (int e = tid; e < MOE_MAX_EXPERTS; e += CAP_THREADS_) fill[e] = 0;
+    for (int i = tid; i < CAP_WAVES_ * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&cnt[0][0])[i] = 0u;
+    uint32_t round = 0;                   // stamps of cnt; never reused without clearing
+
+    // next chunk's state of this thread's token, fetched during the current chunk: its ranked
+    // row, the first four experts it already holds and the rank after its previous slot's pick
+    u32x4 pre[NVMAX];
+    int ph0 = -1, ph1 = -1, ph2 = -1, ph3 = -1, pstart = 0;
+    auto prefetch = [&](int t_next, int j_next) {
+        if (tid >= CT || t_next >= T) return;
+#pragma unroll
+        for (int i = 0; i < NVMAX; ++i)
+            if (i < NV) pre[i] = ((const u32x4*)(ranked + (size_t)t_next * NP))[i];
+        const int32_t* ir = idx + (size_t)t_next * k;
+        ph0 = j_next > 0 ? ir[0] : -1;
+        ph1 = j_next > 1 ? ir[1] : -1;
+        ph2 = j_next > 2 ? ir[2] : -1;
+        ph3 = j_next > 3 ? ir[3] : -1;
+        pstart = j_next > 0 ? rpos[t_next] : 0;
+    };
+    const int nchunks = (T + CT - 1) / CT;
+    prefetch(tid, 0);
     __syncthreads();
 
     for (int j = 0; j < k; ++j) {
-        for (int c0 = 0; c0 < T; c0 += CAP_THREADS) {
+        for (int ci = 0; ci < nchunks; ++ci) {
+            const int c0 = ci * CT;
             const int t = c0 + tid;
-            const bool active = t < T;
+            const bool active = tid < CT && t < T;
+            if (active) {
 #pragma unroll
-            for (int q = 0; q < MOE_MAX_EXPERTS / 32; ++q) held[q][tid] = 0u;
-            if (active)
-                for (int jj = 0; jj < j; ++jj) {
-                    const int e = idx[(size_t)t * k + jj];
-                    if (e >= 0) held[e >> 5][tid] |= 1u << (e & 31);
-                }
-            for (int e = tid; e < N; e += CAP_THREADS) tau[e] = 0x7FFFFFFF;
+                for (int i = 0; i < NVMAX; ++i)
+                    if (i < NV) {
+                        rk4[(4 * i + 0) * CT + tid] = pre[i][0];
+                        rk4[(4 * i + 1) * CT + tid] = pre[i][1];
+                        rk4[(4 * i + 2) * CT + tid] = pre[i][2];
+                        rk4[(4 * i + 3) * CT + tid] = pre[i][3];
+                    }
+            }
+            const int h0 = ph0, h1 = ph1, h2 = ph2, h3 = ph3;
+            // the rank after the previous slot's pick: everything ranked above it was held or
+            // full then, and fills never go down
+            const int start = pstart;
+            for (int e = tid; e < MOE_MAX_EXPERTS; e += CAP_THREADS_) {
+                tau[e] = 0x7FFFFFFF;
+                roomb[e] = (e < N && fill[e] < C) ? 1 : 0;
+            }
             __syncthreads();
-            int ptr = 0, choice = -1;
+            // next: the following chunk of this pass (the first chunk of the next pass is fetched
+            // once this chunk's picks are written: with a single chunk they are its own tokens)
+            if (ci + 1 < nchunks) prefetch(t + CT, j);
+            int q = start >> 2, bpos = start & 3, choice = -1;
             bool choose = active;
-            int total_e = 0;  // thread e < N: proposers of e in the last round
             while (true) {
-                if (choose) {
+                ++round;
+                if (choose) {                             // next candidate from (q, bpos) on
                     choice = -1;
-                    const uint8_t* rk = ranked + (size_t)t * N;
-                    while (ptr < N) {
-                        const int e = rk[ptr];
-                        if (!((held[e >> 5][tid] >> (e & 31)) & 1u) && fill[e] < C && t <= tau[e]) {
+                    while (q < NQ) {
+                        const uint32_t wd = rk4[q * CT + tid];
+                        // room flags of the word's four experts, one bit each
+                        const uint32_t rf = (uint32_t)roomb[wd & 0xFF] | ((uint32_t)roomb[(wd >> 8) & 0xFF] << 1) |
+                                            ((uint32_t)roomb[(wd >> 16) & 0xFF] << 2) |
+                                            ((uint32_t)roomb[wd >> 24] << 3);
+                        if ((rf >> bpos) == 0) {                              // nothing left here
+                            ++q;
+                            bpos = 0;
+                            continue;
+                        }
+                        for (; bpos < 4; ++bpos) {
+                            const int e = (wd >> (8 * bpos)) & 0xFF;
+                            if (!((rf >> bpos) & 1u)) continue;              // full at chunk start
+                            if (t > tau[e]) continue;                         // turned away this chunk
+                            bool held = e == h0 || e == h1 || e == h2 || e == h3;
+                            for (int jj = 4; jj < j && !held; ++jj) held = idx[(size_t)t * k + jj] == e;
+                            if (held) continue;
                             choice = e;
                             break;
                         }
-                        ++ptr;
+                        if (choice >= 0) break;
+                        ++q;
+                        bpos = 0;
                     }
                     choose = false;
                 }
-                for (int i = tid; i < CAP_WAVES * MOE_MAX_EXPERTS; i += CAP_THREADS)
-                    (&wcnt[0][0])[i] = 0;
-                __syncthreads();
-                // rank of this proposal among the wave's proposals to the same expert
-                const uint32_t v = (uint32_t)(choice + 1);  // 0 = no proposal
+                // per-wave proposal counts (ballot matching), written once per expert and wave
+                const uint32_t v = (uint32_t)(choice + 1);
                 const uint64_t eq = match_lanes<9>(v);
                 const int rin = __popcll(eq & lanemask_lt());
-                if (choice >= 0 && rin == 0) wcnt[wave][choice] = __popcll(eq);
-                __syncthreads();
-                if (tid < N) {  // exclusive prefix over waves, per expert
-                    int s = 0;
-                    for (int ww = 0; ww < CAP_WAVES; ++ww) {
-                        const int c = wcnt[ww][tid];
-                        wcnt[ww][tid] = s;
-                        s += c;
-                    }
-                    total_e = s;
-                }
+                if (choice >= 0 && rin == 0) cnt[wave][choice] = (round << 16) | (uint32_t)__popcll(eq);
                 __syncthreads();
                 bool rejected = false;
                 if (choice >= 0) {
-                    const int rank = wcnt[wave][choice] + rin;
+                    int rank = rin;
+                    for (int ww = 0; ww < wave; ++ww) {
+                        const uint32_t c = cnt[ww][choice];
+                        rank += (c >> 16) == round ? (int)(c & 0xFFFF) : 0;
+                    }
                     const int room = C - fill[choice];
                     if (rank == room - 1) tau[choice] = t;
                     if (rank >= room) {
                         rejected = true;
-                        ++ptr;
+                        if (++bpos == 4) { bpos = 0; ++q; }
                         choose = true;
                     }
                 }
                 if (!__syncthreads_or(rejected)) break;
             }
-            if (active) idx[(size_t)t * k + j] = choice;
-            if (tid < N) fill[tid] += total_e;  // at the fixed point every proposal is kept
+            if (active) {
+                idx[(size_t)t * k + j] = choice;
+                rpos[t] = (uint8_t)(choice >= 0 ? (q * 4 + bpos + 1 < 256 ? q * 4 + bpos + 1 : 255) : 255);
+            }
+            if (ci + 1 == nchunks && j + 1 < k) prefetch(tid, j + 1);
+            if (tid < N) {                                // at the fixed point every proposal is kept
+                int s = 0;
+                for (int ww = 0; ww < CAP_WAVES_; ++ww) {
+                    const uint32_t c = cnt[ww][tid];
+                    s += (c >> 16) == round ? (int)(c & 0xFFFF) : 0;
+                }
+                fill[tid] += s;
+            }
+            if (round >= 0xFFF0) {                        // keep stamps unique: clear and restart
+                __syncthreads();
+                for (int i = tid; i < CAP_WAVES_ * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&cnt[0][0])[i] = 0u;
+                round = 0;
+            }
             __syncthreads();
         }
     }
-    // gate weights over the final experts
-    for (int t = tid; t < T; t += CAP_THREADS) {
-        const float* zr = z + (size_t)t * N;
-        int32_t* ir = idx + (size_t)t * k;
-        float* wrow = w + (size_t)t * k;
-        float zmax = -INFINITY;
-        if (gating == 1) {
-            for (int e = 0; e < N; ++e) zmax = fmaxf(zmax, zr[e]);
-        } else {
-            for (int j = 0; j < k; ++j)
-                if (ir[j] >= 0) zmax = fmaxf(zmax, zr[ir[j]]);
-        }
-        float denom = 0.f;
-        if (gating == 1) {
-            for (int e = 0; e < N; ++e) denom += __expf(zr[e] - zmax);
-        } else {
-            for (int j = 0; j < k; ++j)
-                if (ir[j] >= 0) denom += __expf(zr[ir[j]] - zmax);
-        }
-        for (int j = 0; j < k; ++j)
-            wrow[j] = ir[j] >= 0 ? __expf(zr[ir[j]] - zmax) / denom : 0.f;
+}
+
+// Gate weights of routed slots (idx -1 = dropped, weight 0), one wave per token.  Mode 0:
+// softmax over the kept slots' logits; mode 1: softmax over all N logits taken at the slots.
+__global__ __launch_bounds__(256) void slot_gate_kernel(const float* __restrict__ z,
+                                                        const int32_t* __restrict__ idx, int T, int N,
+                                                        int k, int gating, float* __restrict__ w) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const float* zr = z + (size_t)t * N;
+    const int32_t* ir = idx + (size_t)t * k;
+    float zmax = -INFINITY, denom = 0.f;
+    if (gating == 1) {
+        for (int e = lane; e < N; e += 64) zmax = fmaxf(zmax, zr[e]);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, m, 64));
+        float s = 0.f;
+        for (int e = lane; e < N; e += 64) s += __expf(zr[e] - zmax);
+        denom = wave_sum_f32(s);
+    } else {
+        for (int j = lane; j < k; j += 64)
+            if (ir[j] >= 0) zmax = fmaxf(zmax, zr[ir[j]]);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, m, 64));
+        float s = 0.f;
+        for (int j = lane; j < k; j += 64)
+            if (ir[j] >= 0) s += __expf(zr[ir[j]] - zmax);
+        denom = wave_sum_f32(s);
+    }
+    for (int j = lane; j < k; j += 64) {
+        const int e = ir[j];
+        w[(size_t)t * k + j] = e >= 0 ? __expf(zr[e] - zmax) / denom : 0.f;
     }
 }
 
@@ -334,13 +422,29 @@ hipError_t launch_topk_gate(const float* z, int T, int N, int k, int gating, int
     return hipGetLastError();
 }
 
+int capacity_ranked_stride(int N) { return (N + 15) & ~15; }
+size_t capacity_workspace_bytes(int T, int N) { return (size_t)T * capacity_ranked_stride(N) + (size_t)T; }
+
 hipError_t launch_capacity(const float* z, uint8_t* ranked, int T, int N, int k, int C, int gating,
                            int32_t* idx, float* w, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL(rank_sort_kernel, dim3(T), dim3(64), 0, s, z, T, N, ranked);
+    const int NP = capacity_ranked_stride(N);
+    hipLaunchKernelGGL(rank_sort_kernel, dim3(T), dim3(64), 0, s, z, T, N, NP, ranked);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(capacity_kernel, dim3(1), dim3(CAP_THREADS), 0, s, ranked, z, T, N, k, C,
-                       gating, idx, w);
+    // tokens per chunk: as many as the 96 KiB ranked-list buffer holds, a multiple of 64, at most
+    // one per thread
+    const int threads = NP <= 128 ? 1024 : 512;
+    int CT = (CAP_RK_WORDS / (NP / 4)) & ~63;
+    CT = CT > threads ? threads : CT;
+    if (NP <= 128)
+        hipLaunchKernelGGL((capacity_kernel<8, 1024>), dim3(1), dim3(1024), 0, s, ranked, ranked + (size_t)T * NP,
+                           T, N, NP, CT, k, C, idx);
+    else
+        hipLaunchKernelGGL((capacity_kernel<16, 512>), dim3(1), dim3(512), 0, s, ranked, ranked + (size_t)T * NP,
+                           T, N, NP, CT, k, C, idx);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(slot_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, z, idx, T, N, k, gating, w);
     return hipGetLastError();
 }
