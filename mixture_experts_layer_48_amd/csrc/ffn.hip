@@ -79,6 +79,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     __shared__ __attribute__((aligned(1024))) bf16 st0[ROWS * 64];
     __shared__ __attribute__((aligned(1024))) bf16 st1[ROWS * 64];
     __shared__ int s_info[4];
+    __shared__ float s_scale[MODE == MODE_OUT ? BM : 1];   // gate weight of each row of the tile
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go to M0
@@ -180,58 +181,48 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     const char* baseB0 = (const char*)B0;
     const char* baseB1 = (const char*)(NB == 2 ? B1 : B0);
     const int wm = wave / WGN, wn = wave % WGN;
-    f32x16 acc[NB][TM][TN];
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
-
     // fragment addresses: rows of one wave's fragments differ by multiples of 32, so their
     // swizzle only depends on the lane: row r, chunk c sits at r*64 + ((c ^ ((r >> 1) & 7)) << 3)
     const int fr = lane & 31, fh = lane >> 5, l7 = (fr >> 1) & 7;
-    const int abase = (wm * Cfg::WTM + fr) * 64;
+    const int abase = (wm * 32 + fr) * 64;              // sub-tile i of this wave: i * WGM + wm
     const int bbase = (BM + wn * Cfg::WTN + fr) * 64;
     struct Frags { bf16x8 a[TM]; bf16x8 b[NB][TN]; };
-    auto load_frags = [&](const bf16* st, int kk, Frags& f) {
+    auto load_frags = [&](const bf16* st, int kk, Frags& f, auto nv) {
         const int xo = ((2 * kk + fh) ^ l7) << 3;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) f.a[i] = *(const bf16x8*)(st + abase + i * 32 * 64 + xo);
+        for (int i = 0; i < decltype(nv)::value; ++i)
+            f.a[i] = *(const bf16x8*)(st + abase + i * WGM * 32 * 64 + xo);
 #pragma unroll
         for (int m = 0; m < NB; ++m)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 f.b[m][j] = *(const bf16x8*)(st + bbase + (m * BNH + j * 32) * 64 + xo);
     };
-    // rows of this tile that exist; a tile short of BM rows (an expert's last one) skips the
-    // MFMAs of its empty 32-row sub-tiles, so it finishes early and frees its CU
+    // The tile's 32-row sub-tiles are dealt to the wave rows in turn (sub-tile s to wave row
+    // s % WGM), so the rows of a short tile (an expert's last one) spread over all waves.  A tile
+    // whose valid sub-tiles fit in NV per wave runs the variant with NV sub-tiles per wave and
+    // skips the MFMAs and fragment reads of the rest; rows past the end were loaded as copies of
+    // the first row and are never stored.
     const int rows_valid = row_end - m0;
-    const bool full_tile = rows_valid >= BM;
-    int nvi = (rows_valid - wm * Cfg::WTM + 31) / 32;
-    nvi = nvi < 0 ? 0 : (nvi > TM ? TM : nvi);
-    auto mfmas = [&](const Frags& f, auto full) {
+    const int nsub = (rows_valid + 31) / 32;
+    typedef f32x16 Acc[NB][TM][TN];
+    auto mfmas = [&](Acc& acc, const Frags& f, auto nv) {
 #pragma unroll
         for (int m = 0; m < NB; ++m)
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                if (!decltype(full)::value && i >= nvi) continue;
+            for (int i = 0; i < decltype(nv)::value; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[m][j],
                                                                           acc[m][i][j], 0, 0, 0);
             }
     };
-    constexpr int NMF = NB * TM * TN;            // MFMAs per K=16 step
-    constexpr int NDS = TM + NB * TN;            // fragment reads per K=16 step
     constexpr int NLD = A_INS + B_INS;           // direct-to-LDS loads per stage
     constexpr int NLD0 = (NLD + 1) / 2;          // ... issued during step 0, the rest during step 1
     // Interleave one MFMA with the step's other instructions so that a single wave per SIMD keeps
     // the matrix core busy: MFMA, fragment read, MFMA, load, ...
-    auto interleave = [&](int n_ds, int n_ld, auto full) {
-        if (!decltype(full)::value) return;   // partial tiles: leave the order to the compiler
+    auto interleave = [&](int n_ds, int n_ld, auto nv) {
+        constexpr int NMF = NB * decltype(nv)::value * TN;   // MFMAs per K=16 step
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
@@ -264,74 +255,195 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     // MFMAs run, and step 3 already sends the first half of the stage after next into the slot
     // this stage has just released.  Loads past the last stage re-read K offset 0 into the idle
     // slot (in bounds, never used), which keeps the schedule free of branches.
-    auto stage = [&](bf16* cur, bf16* nxt, int k_next, int k_after, Frags& f0, Frags& f1, auto full) {
-        load_frags(cur, 1, f1);
+    auto stage = [&](Acc& acc, bf16* cur, bf16* nxt, int k_next, int k_after, Frags& f0, Frags& f1, auto nv) {
+        constexpr int NDS = decltype(nv)::value + NB * TN;   // fragment reads per K=16 step
+        load_frags(cur, 1, f1, nv);
         issue_part(nxt, k_next, NLD0, NLD);
-        mfmas(f0, full);
-        interleave(NDS, NLD - NLD0, full);
+        mfmas(acc, f0, nv);
+        interleave(NDS, NLD - NLD0, nv);
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(cur, 2, f0);
-        mfmas(f1, full);
-        interleave(NDS, 0, full);
+        load_frags(cur, 2, f0, nv);
+        mfmas(acc, f1, nv);
+        interleave(NDS, 0, nv);
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(cur, 3, f1);
-        mfmas(f0, full);
-        interleave(NDS, 0, full);
+        load_frags(cur, 3, f1, nv);
+        mfmas(acc, f0, nv);
+        interleave(NDS, 0, nv);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0x0070);    // vmcnt(0) lgkmcnt(0): own loads and reads done
         __syncthreads();                       // next stage visible; this stage no longer read
-        load_frags(nxt, 0, f0);
+        load_frags(nxt, 0, f0, nv);
         issue_part(cur, k_after, 0, NLD0);
-        mfmas(f1, full);
-        interleave(NDS, NLD0, full);
+        mfmas(acc, f1, nv);
+        interleave(NDS, NLD0, nv);
         __builtin_amdgcn_sched_barrier(0);
     };
 
     const int KT = a.K / FB_BK / a.ksplit;                 // stages of this K part
     const int kbase = kpart * KT * FB_BK;
     auto kofs = [&](int t) { return kbase + (t < KT ? t : 0) * FB_BK; };
-    auto run = [&](auto full) {
+    // Epilogue.  32x32 C layout: lane holds column (lane & 31); register r holds row
+    // 8*(r >> 2) + 4*(lane >> 5) + (r & 3).
+    auto store = [&](const Acc& acc, auto nv) {
+#pragma unroll
+        for (int i = 0; i < decltype(nv)::value; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + (i * WGM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row >= row_end) continue;
+                const float scale = (MODE == MODE_OUT) ? s_scale[row - m0] : 1.0f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
+                    if (col >= a.Ncols) continue;
+                    float v;
+                    if (MODE == MODE_IN_SWIGLU) v = silu_f32(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
+                    else if (MODE == MODE_IN_RELU) v = fmaxf(acc[0][i][j][r], 0.f);
+                    else v = acc[0][i][j][r] * scale;
+                    if (MODE == MODE_OUT) ((float*)a.C)[kpart * a.part_stride + (size_t)row * a.Ncols + col] = v;
+                    else ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)v;
+                }
+            }
+        }
+    };
+    // Each variant owns its accumulators and epilogue, so no accumulator is live across the
+    // choice of variant.
+    auto run = [&](auto nv) {
+        Acc acc;
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
         Frags fa, fb;
+        // the out-projection's row scales are fetched once per tile, while the first stage loads
+        float sc = 1.0f;
+        if (MODE == MODE_OUT && tid < BM && m0 + tid < row_end && a.row_scale && seg < a.N)
+            sc = a.row_scale[a.perm[m0 + tid]];
         issue_part(st0, kbase, 0, NLD);
         __builtin_amdgcn_s_waitcnt(0x0070);
+        if (MODE == MODE_OUT && tid < BM) s_scale[tid] = sc;
         __syncthreads();
-        load_frags(st0, 0, fa);
+        load_frags(st0, 0, fa, nv);
         issue_part(st1, kofs(1), 0, NLD0);
         int kt = 0;
         for (; kt + 2 <= KT; kt += 2) {
-            stage(st0, st1, kofs(kt + 1), kofs(kt + 2), fa, fb, full);
-            stage(st1, st0, kofs(kt + 2), kofs(kt + 3), fa, fb, full);
+            stage(acc, st0, st1, kofs(kt + 1), kofs(kt + 2), fa, fb, nv);
+            stage(acc, st1, st0, kofs(kt + 2), kofs(kt + 3), fa, fb, nv);
         }
-        if (kt < KT) stage(st0, st1, kbase, kbase, fa, fb, full);
+        if (kt < KT) stage(acc, st0, st1, kbase, kbase, fa, fb, nv);
         __builtin_amdgcn_s_waitcnt(0x0070);    // no load may still be writing LDS at exit
+        store(acc, nv);
     };
-    if (full_tile) run(std::true_type{});
-    else run(std::false_type{});
+    if (TM >= 2 && nsub <= WGM) run(std::integral_constant<int, 1>{});
+    else if (TM >= 4 && nsub <= 2 * WGM) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, TM>{});
+}
 
-    // epilogue.  32x32 C layout: lane holds column (lane & 31); register r holds row
-    // 8*(r >> 2) + 4*(lane >> 5) + (r & 3).
+// ------------------------------------------------------------------ skinny path (decode)
+// For a few rows per expert the GEMMs are weight streams: every weight byte of a touched expert
+// is read once and used for at most 16 rows.  One wave owns one 16-column group of one segment
+// and the whole K range; its B fragments (16 weight rows x 32 K for v_mfma_f32_16x16x32_bf16)
+// come straight from memory into registers, several steps ahead, and its A fragments (the <= 16
+// rows, gathered through perm for the in-projection) are shared by all waves through L2.  Empty
+// experts are skipped, so only touched experts' weights are read.  Segments with more than 16
+// rows loop over 16-row tiles.
+#define SK_UNROLL 8
+
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
+    constexpr int NB = (MODE == MODE_IN_SWIGLU) ? 2 : 1;
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);        // global wave id
+    const int ngroups = (a.Ncols + 15) / 16;
+    const int nseg = a.N + (a.has_shared ? 1 : 0);
+    const int seg = gw / ngroups, cg = gw % ngroups;
+    if (seg >= nseg) return;
+    int row_beg, row_end;
+    const bf16 *B0, *B1 = nullptr;
+    const size_t wstride = (size_t)a.Ncols * a.K;
+    if (seg < a.N) {
+        row_beg = a.offsets[seg];
+        row_end = a.offsets[seg + 1];
+        B0 = a.B0 + seg * wstride;
+        if (NB == 2) B1 = a.B1 + seg * wstride;
+    } else {
+        row_beg = a.T * a.k;
+        row_end = row_beg + a.T;
+        B0 = a.S0;
+        if (NB == 2) B1 = a.S1;
+    }
+    if (row_end <= row_beg) return;                             // expert not touched
+    const int col = cg * 16 + (lane & 15);                      // this lane's B column
+    const int colc = col < a.Ncols ? col : a.Ncols - 1;
+    const int kq = (lane >> 4) * 8;                             // this lane's K offset in a step
+    const bf16* pb0 = B0 + (size_t)colc * a.K + kq;
+    const bf16* pb1 = (NB == 2) ? B1 + (size_t)colc * a.K + kq : nullptr;
+    const int KS = a.K / 32;
+    for (int m0 = row_beg; m0 < row_end; m0 += 16) {
+        const int r = m0 + (lane & 15);                         // this lane's A row
+        const bool rok = r < row_end;
+        int src;
+        if (MODE == MODE_OUT) src = rok ? r : m0;
+        else src = (seg < a.N) ? a.perm[rok ? r : m0] / a.k : (rok ? r : m0) - a.T * a.k;
+        const bf16* pa = a.A + (size_t)src * a.K + kq;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        const bf16x8 zero8 = {};
+        int ks = 0;
+        for (; ks + SK_UNROLL <= KS; ks += SK_UNROLL) {
+            bf16x8 b0[SK_UNROLL], b1[SK_UNROLL], av[SK_UNROLL];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+            for (int u = 0; u < SK_UNROLL; ++u) {
+                b0[u] = *(const bf16x8*)(pb0 + (ks + u) * 32);
+                if (NB == 2) b1[u] = *(const bf16x8*)(pb1 + (ks + u) * 32);
+                av[u] = rok ? *(const bf16x8*)(pa + (ks + u) * 32) : zero8;
+            }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * Cfg::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row >= row_end) continue;
-            float scale = 1.0f;
-            if (MODE == MODE_OUT && a.row_scale && seg < a.N) scale = a.row_scale[a.perm[row]];
+            for (int u = 0; u < SK_UNROLL; ++u) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b0[u], acc0, 0, 0, 0);
+                if (NB == 2) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b1[u], acc1, 0, 0, 0);
+            }
+        }
+        for (; ks < KS; ++ks) {
+            const bf16x8 b0 = *(const bf16x8*)(pb0 + ks * 32);
+            const bf16x8 av = rok ? *(const bf16x8*)(pa + ks * 32) : zero8;
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0, acc0, 0, 0, 0);
+            if (NB == 2) {
+                const bf16x8 b1 = *(const bf16x8*)(pb1 + ks * 32);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1, acc1, 0, 0, 0);
+            }
+        }
+        // 16x16 C layout: lane holds column (lane & 15), rows 4 * (lane >> 4) + i
+        if (col < a.Ncols) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
-                if (col >= a.Ncols) continue;
-                float v;
-                if (MODE == MODE_IN_SWIGLU) v = silu_f32(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
-                else if (MODE == MODE_IN_RELU) v = fmaxf(acc[0][i][j][r], 0.f);
-                else v = acc[0][i][j][r] * scale;
-                if (MODE == MODE_OUT) ((float*)a.C)[kpart * a.part_stride + (size_t)row * a.Ncols + col] = v;
-                else ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)v;
+            for (int i = 0; i < 4; ++i) {
+                const int row = m0 + 4 * (lane >> 4) + i;
+                if (row >= row_end) continue;
+                if (MODE == MODE_OUT) {
+                    const float scale = (a.row_scale && seg < a.N) ? a.row_scale[a.perm[row]] : 1.0f;
+                    ((float*)a.C)[(size_t)row * a.Ncols + col] = acc0[i] * scale;
+                } else if (MODE == MODE_IN_SWIGLU) {
+                    ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)(silu_f32(acc0[i]) * acc1[i]);
+                } else {
+                    ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)fmaxf(acc0[i], 0.f);
+                }
             }
         }
     }
 }
+
+template <int MODE>
+static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
+    const long long waves = (long long)(a.N + (a.has_shared ? 1 : 0)) * ((a.Ncols + 15) / 16);
+    hipLaunchKernelGGL(ffn_skinny_kernel<MODE>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// Decode-sized batches (at most 16 rows per expert on average) take the weight-streaming path.
+static bool skinny(const FfnLaunch& f) { return (long long)f.T * f.k <= 16LL * f.N; }
 
 // ------------------------------------------------------------------ fp32 path
 // One thread per output element, fp32 FMA in input order.  Used for fp32 layers.
@@ -430,11 +542,13 @@ hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
         if (f.ffn == 1) {
             a.B0 = (const bf16*)f.w_gate; a.B1 = (const bf16*)f.w_up;
             a.S0 = (const bf16*)f.sh_gate; a.S1 = (const bf16*)f.sh_up;
+            if (skinny(f)) return launch_skinny<MODE_IN_SWIGLU>(a, s);
             if (big_tiles(f)) return launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, s);
             return launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, s);
         }
         a.B0 = (const bf16*)f.w_up;
         a.S0 = (const bf16*)f.sh_up;
+        if (skinny(f)) return launch_skinny<MODE_IN_RELU>(a, s);
         if (big_tiles(f)) return launch_bf16<MODE_IN_RELU, 256, 256, 2, 2>(a, s);
         return launch_bf16<MODE_IN_RELU, 128, 128, 2, 2>(a, s);
     }
@@ -466,6 +580,7 @@ hipError_t launch_ffn_out(const FfnLaunch& f, hipStream_t s) {
         a.K = f.d_ff; a.Ncols = f.d;
         a.ksplit = f.ksplit;
         a.part_stride = (long long)((long long)f.T * f.k + (f.has_shared ? f.T : 0)) * f.d;
+        if (skinny(f)) return launch_skinny<MODE_OUT>(a, s);
         if (big_tiles(f)) return launch_bf16<MODE_OUT, 256, 256, 2, 2>(a, s);
         return launch_bf16<MODE_OUT, 128, 128, 2, 2>(a, s);
     }

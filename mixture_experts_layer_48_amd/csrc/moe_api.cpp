@@ -6,6 +6,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdio>
+#include <algorithm>
 #include <string>
 
 #include "../../include/moe.h"
@@ -95,7 +96,9 @@ Layout layout_of(const moe_layer_desc& d) {
     L.offsets = o; o += align256((N + 1) * 4);
     L.perm = o; o += align256(T * k * 4);
     L.inv = o; o += align256(T * k * 4);
-    L.h = o; o += align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d));
+    // the router's partial logits are dead before the hidden state is written: they share space
+    L.h = o; o += std::max(align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d)),
+                           align256(router_workspace_bytes(d.T, d.d, d.N, d.dtype)));
     // fp32 expert rows, one copy per K part of the out-projection
     L.yp = o; o += align256((size_t)rows_total(d) * d.d * 4 * ksplit_of(d));
     L.total = o;
@@ -103,7 +106,8 @@ Layout layout_of(const moe_layer_desc& d) {
 }
 size_t route_ws_bytes(const moe_layer_desc& d, bool have_logits) {
     return (have_logits ? 0 : align256((size_t)d.T * d.N * 4)) +
-           (has_capacity(d) ? align256(capacity_workspace_bytes(d.T, d.N)) : 0);
+           (has_capacity(d) ? align256(capacity_workspace_bytes(d.T, d.N)) : 0) +
+           align256(router_workspace_bytes(d.T, d.d, d.N, d.dtype));
 }
 size_t ffn_ws_bytes(const moe_layer_desc& d) {
     return align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d));
@@ -113,8 +117,9 @@ char* at(void* ws, size_t off) { return (char*)ws + off; }
 
 // ---- stages (arguments already validated)
 moe_status stage_route(const moe_layer_desc& d, const void* x, const void* wr, const float* bias, float* z,
-                       uint8_t* ranked, int32_t* idx, float* w, hipStream_t s, hipEvent_t ev_mid) {
-    hipError_t e = launch_router_logits(x, wr, bias, z, d.T, d.d, d.N, d.dtype, s);
+                       void* rpart, uint8_t* ranked, int32_t* idx, float* w, hipStream_t s,
+                       hipEvent_t ev_mid) {
+    hipError_t e = launch_router_logits(x, wr, bias, z, rpart, d.T, d.d, d.N, d.dtype, s);
     if (e != hipSuccess) return hip_fail(e, "router logits launch");
     if (!has_capacity(d)) {
         e = launch_topk_gate(z, d.T, d.N, d.k, d.gating, idx, w, s);
@@ -174,8 +179,10 @@ moe_status moe_route(const moe_layer_desc* desc, const void* x, const void* w_ro
     size_t o = 0;
     float* z = logits;
     if (!z) { z = (float*)at(ws, o); o += align256((size_t)d.T * d.N * 4); }
-    uint8_t* ranked = has_capacity(d) ? (uint8_t*)at(ws, o) : nullptr;
-    return stage_route(d, x, w_router, logit_bias, z, ranked, idx, w, (hipStream_t)stream, nullptr);
+    uint8_t* ranked = nullptr;
+    if (has_capacity(d)) { ranked = (uint8_t*)at(ws, o); o += align256(capacity_workspace_bytes(d.T, d.N)); }
+    void* rpart = router_workspace_bytes(d.T, d.d, d.N, d.dtype) ? at(ws, o) : nullptr;
+    return stage_route(d, x, w_router, logit_bias, z, rpart, ranked, idx, w, (hipStream_t)stream, nullptr);
 }
 
 moe_status moe_permute(const moe_layer_desc* desc, const int32_t* idx, int32_t* counts, int32_t* offsets,
@@ -265,7 +272,8 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_weights
     void* yp = at(ws, L.yp);
 
     if ((st = record(ev(0), s)) != MOE_OK) return st;
-    st = stage_route(d, x, weights->w_router, weights->logit_bias, z, (uint8_t*)at(ws, L.ranked), idx, w, s, ev(1));
+    st = stage_route(d, x, weights->w_router, weights->logit_bias, z, at(ws, L.h), (uint8_t*)at(ws, L.ranked),
+                     idx, w, s, ev(1));
     if (st != MOE_OK) return st;
     if ((st = record(ev(2), s)) != MOE_OK) return st;
     hipError_t e = launch_permute(idx, d.T, d.k, d.N, counts, offsets, perm, inv, s);

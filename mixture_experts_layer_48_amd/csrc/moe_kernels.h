@@ -4,8 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, float* z, int T,
-                                int d, int N, int dtype, hipStream_t s);
+// workspace of the router: fp64 partial logits [K parts, T, N] when K is split, else nothing
+size_t router_workspace_bytes(int T, int d, int N, int dtype);
+hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, float* z, void* ws,
+                                int T, int d, int N, int dtype, hipStream_t s);
 hipError_t launch_topk_gate(const float* z, int T, int N, int k, int gating, int32_t* idx, float* w,
                             hipStream_t s);
 // workspace of the capacity step: ranked lists [T, capacity_ranked_stride(N)] bytes, then [T]

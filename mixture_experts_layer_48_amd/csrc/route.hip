@@ -11,22 +11,77 @@
 #include "moe_kernels.h"
 
 // ------------------------------------------------------------------ router logits, bf16 (MFMA)
-// Block = 4 waves; block tile = 128 tokens x 64 experts; wave w owns tokens [32w, 32w+32) of the
-// tile and all 64 experts (4 MFMA column tiles of 16, 2 row tiles of 16).  Products are summed
-// by v_mfma_f32_16x16x32_bf16 into fp32 over chunks of 256 inputs, and the chunk sums are added
-// in fp64, which keeps the logit error far below the gaps that decide the ranking.  The final
-// logit (plus bias, in fp64) is rounded once to fp32.
-#define RL_BM 128
+// Work unit = one wave: 32 tokens (2 MFMA row tiles of 16) x 64 experts (4 column tiles of 16) x
+// one range of K.  Products are summed by v_mfma_f32_16x16x32_bf16 into fp32 over chunks of 256
+// inputs and the chunk sums are added in fp64, which keeps the logit error far below the gaps
+// that decide the ranking.  When the grid would be too small to fill the chip (few tokens or
+// experts) K is split into parts: each part's fp64 sum goes to the workspace and a second kernel
+// adds the parts in part order plus the bias; otherwise the unit adds the bias and writes the
+// logit, rounded once to fp32.  Units are numbered expert tile fastest, so the waves of one block
+// share their token rows through the cache.
+#define RL_BM 32
 #define RL_BN 64
 #define RL_CHUNK 256
+#define RL_TARGET_WAVES 2048
+
+struct RouterSplit {
+    int n_tt, n_et, nchunks, ks, cpp;   // token tiles, expert tiles, chunks, K parts, chunks per part
+};
+static RouterSplit router_split(int T, int d, int N) {
+    RouterSplit r;
+    r.n_tt = (T + RL_BM - 1) / RL_BM;
+    r.n_et = (N + RL_BN - 1) / RL_BN;
+    r.nchunks = (d + RL_CHUNK - 1) / RL_CHUNK;
+    const long long per_part = (long long)r.n_tt * r.n_et;
+    long long ks = (RL_TARGET_WAVES + per_part - 1) / per_part;
+    if (ks > r.nchunks) ks = r.nchunks;
+    if (ks < 1) ks = 1;
+    r.cpp = (int)((r.nchunks + ks - 1) / ks);
+    r.ks = (r.nchunks + r.cpp - 1) / r.cpp;
+    return r;
+}
+
+size_t router_workspace_bytes(int T, int d, int N, int dtype) {
+    if (dtype != 1 || T == 0) return 0;
+    const RouterSplit r = router_split(T, d, N);
+    return r.ks > 1 ? (size_t)r.ks * T * N * sizeof(double) : 0;
+}
+
+// NS k-steps of 32: all loads first, then the MFMAs.
+template <int NS>
+__device__ __forceinline__ void router_steps(const bf16* pa0, const bf16* pa1, const bf16* const (&pb)[4],
+                                             bool okA0, bool okA1, const bool (&okB)[4], int nct, int kk,
+                                             f32x4 (&acc)[4][2]) {
+    const bf16x8 zero8 = {};
+    bf16x8 a0[NS], a1[NS], bv[NS][4];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        a0[s] = okA0 ? *(const bf16x8*)(pa0 + kk + 32 * s) : zero8;
+        a1[s] = okA1 ? *(const bf16x8*)(pa1 + kk + 32 * s) : zero8;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (c < nct) bv[s][c] = okB[c] ? *(const bf16x8*)(pb[c] + kk + 32 * s) : zero8;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (c < nct) {
+                acc[c][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[s], bv[s][c], acc[c][0], 0, 0, 0);
+                acc[c][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[s], bv[s][c], acc[c][1], 0, 0, 0);
+            }
+}
 
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ wr, const float* __restrict__ bias,
-    float* __restrict__ z, int T, int d, int N) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t0 = blockIdx.x * RL_BM + wave * 32;
-    const int e0 = blockIdx.y * RL_BN;
-    const int nct = min(4, (N - e0 + 15) >> 4);  // valid 16-wide column tiles (uniform)
+    float* __restrict__ z, double* __restrict__ part, int T, int d, int N, RouterSplit sp) {
+    const int lane = threadIdx.x & 63;
+    const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int et = u % sp.n_et, rest = u / sp.n_et;
+    const int kp = rest % sp.ks, tt = rest / sp.ks;
+    if (tt >= sp.n_tt) return;
+    const int t0 = tt * RL_BM, e0 = et * RL_BN;
+    const int nct = min(4, (N - e0 + 15) >> 4);   // valid 16-wide column tiles (uniform)
     const int koff = (lane >> 4) * 8;
     const int rowA0 = t0 + (lane & 15), rowA1 = rowA0 + 16;
     const bool okA0 = rowA0 < T, okA1 = rowA1 < T;
@@ -48,24 +103,15 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc64[c][r][i] = 0.0;
 
-    const bf16x8 zero8 = {};
-    for (int kc = 0; kc < d; kc += RL_CHUNK) {
+    const int c_beg = kp * sp.cpp, c_end = min(c_beg + sp.cpp, sp.nchunks);
+    for (int ch = c_beg; ch < c_end; ++ch) {
+        const int kc = ch * RL_CHUNK, kend = min(kc + RL_CHUNK, d);
         f32x4 acc[4][2];
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c][0] = acc[c][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        const int kend = min(kc + RL_CHUNK, d);
-        for (int kk = kc; kk < kend; kk += 32) {
-            bf16x8 a0 = okA0 ? *(const bf16x8*)(pa0 + kk) : zero8;
-            bf16x8 a1 = okA1 ? *(const bf16x8*)(pa1 + kk) : zero8;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (c < nct) {
-                    bf16x8 b = okB[c] ? *(const bf16x8*)(pb[c] + kk) : zero8;
-                    acc[c][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[c][0], 0, 0, 0);
-                    acc[c][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[c][1], 0, 0, 0);
-                }
-            }
-        }
+        int kk = kc;
+        for (; kk + 64 <= kend; kk += 64) router_steps<2>(pa0, pa1, pb, okA0, okA1, okB, nct, kk, acc);
+        for (; kk < kend; kk += 32) router_steps<1>(pa0, pa1, pb, okA0, okA1, okB, nct, kk, acc);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -84,9 +130,24 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = t0 + r * 16 + 4 * (lane >> 4) + i;
-                if (t < T) z[(size_t)t * N + e] = (float)(acc64[c][r][i] + b);
+                if (t >= T) continue;
+                if (sp.ks == 1) z[(size_t)t * N + e] = (float)(acc64[c][r][i] + b);
+                else part[((size_t)kp * T + t) * N + e] = acc64[c][r][i];
             }
     }
+}
+
+// Sum of the K parts in part order, plus the bias, rounded once to fp32.
+__global__ __launch_bounds__(256) void router_reduce_kernel(const double* __restrict__ part,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ z, int T, int N, int ks) {
+    const long long o = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long TN = (long long)T * N;
+    if (o >= TN) return;
+    double acc = 0.0;
+    for (int p = 0; p < ks; ++p) acc += part[p * TN + o];
+    if (bias) acc += (double)bias[o % N];
+    z[o] = (float)acc;
 }
 
 // ------------------------------------------------------------------ router logits, fp32
@@ -400,13 +461,19 @@ __global__ __launch_bounds__(256) void slot_gate_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ launchers
-hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, float* z, int T,
-                                int d, int N, int dtype, hipStream_t s) {
+hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, float* z, void* ws,
+                                int T, int d, int N, int dtype, hipStream_t s) {
     if (T == 0) return hipSuccess;
     if (dtype == 1) {
-        dim3 grid((T + RL_BM - 1) / RL_BM, (N + RL_BN - 1) / RL_BN);
-        hipLaunchKernelGGL(router_logits_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)x,
-                           (const bf16*)wr, bias, z, T, d, N);
+        const RouterSplit sp = router_split(T, d, N);
+        const long long units = (long long)sp.n_tt * sp.n_et * sp.ks;
+        hipLaunchKernelGGL(router_logits_bf16_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s,
+                           (const bf16*)x, (const bf16*)wr, bias, z, (double*)ws, T, d, N, sp);
+        if (sp.ks > 1) {
+            const long long n = (long long)T * N;
+            hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                               (const double*)ws, bias, z, T, N, sp.ks);
+        }
     } else {
         const long long n = (long long)T * N;
         hipLaunchKernelGGL(router_logits_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,

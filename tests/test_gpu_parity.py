@@ -58,6 +58,15 @@ SMALL = {
     # long out-projection K: the down projection runs as two K parts summed by the combine
     "split_k_out": W.LayerConfig("split_k_out", T=200, d=128, N=2, k=2, d_ff=8192, dtype="bf16",
                                  ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=17),
+    # at most 16 routed rows per expert on average: the weight-streaming decode GEMMs, here with a
+    # shared expert longer than one 16-row tile, heavy experts, and capacity drops
+    "skinny_relu_shared": W.LayerConfig("skinny_relu_shared", T=24, d=128, N=16, k=2, d_ff=192, dtype="bf16",
+                                        ffn=W.FFN_RELU2, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=18),
+    "skinny_skewed": W.LayerConfig("skinny_skewed", T=100, d=192, N=64, k=4, d_ff=128, dtype="bf16",
+                                   ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, zipf_bias=True, seed=19),
+    "skinny_capacity": W.LayerConfig("skinny_capacity", T=64, d=128, N=16, k=2, d_ff=256, dtype="bf16",
+                                     ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, capacity_factor=1.0,
+                                     zipf_bias=True, seed=20),
 }
 
 
