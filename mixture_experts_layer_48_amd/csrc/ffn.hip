@@ -65,6 +65,57 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 // contiguous in LDS: lane l writes position l & 7 of row 8g + (l >> 3) and therefore fetches
 // chunk (l & 7) ^ ((4g + (l >> 4)) & 7) of that row.
 
+// Work split, computed by wave 0 of every block.  From offsets it counts the real m-tiles of
+// each segment (ceil(rows / BM)); the real tiles are numbered segment by segment, and within a
+// segment n-tile by n-tile with the segment's m-tiles fastest.  The 8 XCDs get equal contiguous
+// ranges of that numbering.  Blocks are dealt to XCDs round-robin (block b runs on XCD b % 8 as
+// its (b / 8)-th block), so the blocks that run together on one XCD are the m-tiles of one expert
+// against neighbouring n-tiles: they share each weight tile and their rows in that XCD's L2, and
+// every XCD gets the same amount of real work.  s_info receives segment (-1: no tile), m-tile,
+// n-tile and K part.
+template <int BM>
+__device__ __forceinline__ void decode_tile(const FfnKArgs& a, int lane, int* s_info) {
+    const int b = blockIdx.x;
+    const int xcd = b & 7, j = b >> 3;
+    int tl[5], loc = 0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+        const int s = lane * 5 + q;
+        int rows = 0;
+        if (s < a.N) rows = a.offsets[s + 1] - a.offsets[s];
+        else if (s == a.N && a.has_shared) rows = a.T;
+        tl[q] = (rows + BM - 1) / BM;
+        loc += tl[q];
+    }
+    int incl = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    const int R1 = __shfl(incl, 63, 64) * a.n_tiles;   // tiles of one K part
+    const int R = R1 * a.ksplit;
+    const int per_xcd = (R + 7) / 8;
+    int t = (j < per_xcd) ? xcd * per_xcd + j : R;     // tile id, R = none
+    const int ks = t < R ? t / R1 : 0;                  // K part (outermost)
+    if (t < R) t -= ks * R1;
+    else t = R1;
+    int run = (incl - loc) * a.n_tiles;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+        const int cnt = tl[q] * a.n_tiles;
+        if (t >= run && t < run + cnt) {
+            const int rem = t - run;
+            s_info[0] = lane * 5 + q;
+            s_info[1] = rem % tl[q];
+            s_info[2] = rem / tl[q];
+        }
+        run += cnt;
+    }
+    if (lane == 63 && t >= R1) s_info[0] = -1;
+    if (lane == 0) s_info[3] = ks;
+}
+
 template <int MODE, int BM, int BNH, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     using Cfg = FfnTile<MODE, BM, BNH, WGM, WGN>;
@@ -83,54 +134,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go to M0
-    // Work split.  Every block computes, from offsets, the real m-tiles of each segment
-    // (ceil(rows / BM)); the real tiles are numbered segment by segment, and within a segment
-    // n-tile by n-tile with the segment's m-tiles fastest.  The 8 XCDs get equal contiguous ranges
-    // of that numbering.  Blocks are dealt to XCDs round-robin (block b runs on XCD b % 8 as its
-    // (b / 8)-th block), so the blocks that run together on one XCD are the m-tiles of one expert
-    // against neighbouring n-tiles: they share each weight tile and their rows in that XCD's L2,
-    // and every XCD gets the same amount of real work.
-    const int b = blockIdx.x;
-    const int xcd = b & 7, j = b >> 3;
-    if (wave == 0) {
-        int tl[5], loc = 0;
-#pragma unroll
-        for (int q = 0; q < 5; ++q) {
-            const int s = lane * 5 + q;
-            int rows = 0;
-            if (s < a.N) rows = a.offsets[s + 1] - a.offsets[s];
-            else if (s == a.N && a.has_shared) rows = a.T;
-            tl[q] = (rows + BM - 1) / BM;
-            loc += tl[q];
-        }
-        int incl = loc;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += v;
-        }
-        const int R1 = __shfl(incl, 63, 64) * a.n_tiles;   // tiles of one K part
-        const int R = R1 * a.ksplit;
-        const int per_xcd = (R + 7) / 8;
-        int t = (j < per_xcd) ? xcd * per_xcd + j : R;     // tile id, R = none
-        const int ks = t < R ? t / R1 : 0;                  // K part (outermost)
-        if (t < R) t -= ks * R1;
-        else t = R1;
-        int run = (incl - loc) * a.n_tiles;
-#pragma unroll
-        for (int q = 0; q < 5; ++q) {
-            const int cnt = tl[q] * a.n_tiles;
-            if (t >= run && t < run + cnt) {
-                const int rem = t - run;
-                s_info[0] = lane * 5 + q;
-                s_info[1] = rem % tl[q];
-                s_info[2] = rem / tl[q];
-            }
-            run += cnt;
-        }
-        if (lane == 63 && t >= R1) s_info[0] = -1;
-        if (lane == 0) s_info[3] = ks;
-    }
+    if (wave == 0) decode_tile<BM>(a, lane, s_info);
     __syncthreads();
     const int seg = s_info[0];
     if (seg < 0) return;

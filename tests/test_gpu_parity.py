@@ -58,6 +58,14 @@ SMALL = {
     # long out-projection K: the down projection runs as two K parts summed by the combine
     "split_k_out": W.LayerConfig("split_k_out", T=200, d=128, N=2, k=2, d_ff=8192, dtype="bf16",
                                  ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=17),
+    # 256-row tiles at real-model K (a multiple of 256): several m-tiles and a short last one;
+    # ReLU with a shared expert; a partial last column tile of the in-projection
+    "tiles256_swiglu": W.LayerConfig("tiles256_swiglu", T=600, d=256, N=2, k=2, d_ff=512, dtype="bf16",
+                                   ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=21),
+    "tiles256_relu_shared": W.LayerConfig("tiles256_relu_shared", T=400, d=512, N=2, k=1, d_ff=768, dtype="bf16",
+                                        ffn=W.FFN_RELU2, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=22),
+    "tiles256_ragged_cols": W.LayerConfig("tiles256_ragged_cols", T=300, d=256, N=1, k=1, d_ff=448, dtype="bf16",
+                                        ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=23),
     # at most 16 routed rows per expert on average: the weight-streaming decode GEMMs, here with a
     # shared expert longer than one 16-row tile, heavy experts, and capacity drops
     "skinny_relu_shared": W.LayerConfig("skinny_relu_shared", T=24, d=128, N=16, k=2, d_ff=192, dtype="bf16",
