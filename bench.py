@@ -18,6 +18,7 @@ import ctypes
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -132,9 +133,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str
     fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write = per_kernel(write_dir, "WRITE_SIZE")
 
-    def pick(d, key):
-        ks = [k for k in d if key in k]
-        return statistics.mean(d[ks[0]]) if ks else float("nan")
+    def pick_in_projection(d):
+        # the gate/up (or W1) kernel: tiled or weight-streaming form, SwiGLU or ReLU mode
+        ks = [k for k in d if re.search(r"ffn_(bf16|skinny)_kernel<[01][,>]", k)]
+        return (statistics.mean(d[ks[0]]), ks[0]) if ks else (float("nan"), "none")
 
     def largest(d, key):
         # the calibration copy is by far the largest copy dispatch of the run
@@ -144,10 +146,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str
     copy_f, copy_w = largest(fetch, "copy"), largest(write, "copy")
     f_scale = copy_bytes / (copy_f * 1024.0)
     w_scale = copy_bytes / (copy_w * 1024.0)
-    ffn_f, ffn_w = pick(fetch, "ffn_bf16_kernel<0"), pick(write, "ffn_bf16_kernel<0")
+    (ffn_f, kname), (ffn_w, _) = pick_in_projection(fetch), pick_in_projection(write)
     hbm = ffn_f * 1024.0 * f_scale + ffn_w * 1024.0 * w_scale
     lines = [
-        f"# HBM traffic of the grouped gate/up projection kernel (ffn_bf16_kernel<0,...>), {workload}",
+        f"# HBM traffic of the grouped in-projection kernel ({kname}), {workload}",
         f"# command: {command}",
         "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by bytes/KiB it reads",
         f"# for a plain device copy of {copy_bytes} bytes in the same run.",
@@ -316,7 +318,7 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         # samples sized for roughly 10-30 s of oracle work on a 16-core host
-        default_sample = {"tiny_fp32": 128, "mixtral_prefill": 1024, "mixtral_decode": 16,
+        default_sample = {"tiny_fp32": 128, "mixtral_prefill": 4096, "mixtral_decode": 16,
                           "deepseek_v3": 256, "skewed_capacity": 2048}.get(cfg.name, 64)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens or default_sample)
     print(json.dumps(out), flush=True)
