@@ -10,8 +10,8 @@
 // worst case (sum over experts of ceil(rows/BM) <= ceil(T*k/BM) + N); each block finds its
 // segment and m-tile on the device from offsets, so the host never reads the routing.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, block tile 128 x 128 (x2 for gate+up), K step 64,
-// LDS double buffer, 4 waves each owning a 64 x 64 quarter.  The in-projection gathers its A
+// bf16 path: v_mfma_f32_32x32x16_bf16, block tiles of 256 or 128 rows, K step 64, LDS double
+// buffer filled by direct loads, 4 waves each owning a quarter of the tile.  The in-projection gathers its A
 // rows straight from x (row = token of the slot), so the permuted copy of x is never built;
 // SwiGLU (silu(g) * u) or ReLU is applied in registers and H is stored in bf16.  The
 // out-projection multiplies each row by its slot's gate weight and stores the row in fp32, so the
@@ -56,7 +56,6 @@ struct FfnTile {
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 // LDS tile layout: rows of 64 bf16 (128 B, 8 chunks of 16 B), unpadded; chunk c of row r sits at
 // position c ^ ((r >> 1) & 7).  A fragment read serves 16 lanes (16 consecutive rows, one chunk,
@@ -65,14 +64,26 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 // contiguous in LDS: lane l writes position l & 7 of row 8g + (l >> 3) and therefore fetches
 // chunk (l & 7) ^ ((4g + (l >> 4)) & 7) of that row.
 
+// 16 bytes per lane from base + voff + soff into LDS (M0 + 16 * lane): the buffer (MUBUF) form
+// of the direct load, with a raw-buffer descriptor (no range limit, 32-bit data format, the gfx9
+// encoding).  The per-lane offset is 32 bits and the K offset goes in a scalar register, so no
+// per-lane 64-bit address arithmetic is needed.  (A function of its own: the host pass drops a
+// kernel whose lambdas use the descriptor type.)
+__device__ __forceinline__ void buffer_load_lds16(const void* base, lds_void_t* dst, uint32_t voff, int soff) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
 // Work split, computed by wave 0 of every block.  From offsets it counts the real m-tiles of
-// each segment (ceil(rows / BM)); the real tiles are numbered segment by segment, and within a
-// segment n-tile by n-tile with the segment's m-tiles fastest.  The 8 XCDs get equal contiguous
-// ranges of that numbering.  Blocks are dealt to XCDs round-robin (block b runs on XCD b % 8 as
-// its (b / 8)-th block), so the blocks that run together on one XCD are the m-tiles of one expert
-// against neighbouring n-tiles: they share each weight tile and their rows in that XCD's L2, and
-// every XCD gets the same amount of real work.  s_info receives segment (-1: no tile), m-tile,
-// n-tile and K part.
+// each segment (ceil(rows / BM)); the real tiles are numbered segment by segment.  Within a
+// segment they go in rectangles of at most 8 m-tiles x (32 / that) n-tiles, m fastest inside a
+// rectangle: 32 blocks are what one XCD runs at once (32 CUs, one block each), so the blocks
+// that run together on an XCD cover a compact rectangle and share its row tiles and weight
+// tiles in that XCD's L2 (a column of 32 m-tiles against one n-tile would fetch every row tile
+// again for every n-tile).  The 8 XCDs get equal contiguous ranges of the numbering; blocks are
+// dealt to XCDs round-robin (block b runs on XCD b % 8 as its (b / 8)-th block), so every XCD
+// gets the same amount of real work.  s_info receives segment (-1: no tile), m-tile, n-tile and
+// K part.
 template <int BM>
 __device__ __forceinline__ void decode_tile(const FfnKArgs& a, int lane, int* s_info) {
     const int b = blockIdx.x;
@@ -105,10 +116,17 @@ __device__ __forceinline__ void decode_tile(const FfnKArgs& a, int lane, int* s_
     for (int q = 0; q < 5; ++q) {
         const int cnt = tl[q] * a.n_tiles;
         if (t >= run && t < run + cnt) {
-            const int rem = t - run;
+            const int rem = t - run, tm = tl[q];
+            const int GM = tm < 8 ? tm : 8;               // m-tiles per rectangle
+            const int GN = 32 / GM;                       // n-tiles per rectangle
+            const int mg = rem / (GM * a.n_tiles);        // rectangle row (GM m-tiles, all n)
+            const int gm = min(GM, tm - mg * GM);         // m-tiles in this row (last may be short)
+            const int r2 = rem - mg * GM * a.n_tiles;
+            const int band = r2 / (gm * GN);              // rectangle within the row
+            const int r3 = r2 - band * gm * GN;
             s_info[0] = lane * 5 + q;
-            s_info[1] = rem % tl[q];
-            s_info[2] = rem / tl[q];
+            s_info[1] = mg * GM + r3 % gm;
+            s_info[2] = band * GN + r3 / gm;
         }
         run += cnt;
     }
@@ -235,21 +253,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         }
     };
     auto issue_part = [&](bf16* st, int k0, int beg, int end) {
-        const char* bA = baseA + 2 * k0;
-        const char* bB0 = baseB0 + 2 * k0;
-        const char* bB1 = baseB1 + 2 * k0;
 #pragma unroll
         for (int q = 0; q < NLD; ++q) {
             if (q < beg || q >= end) continue;
             if (q < A_INS) {
-                __builtin_amdgcn_global_load_lds((gbl_void_t*)(bA + offA[q]),
-                                                 (lds_void_t*)(st + (8 * (wave + NW * q)) * 64), 16, 0, 0);
+                buffer_load_lds16(baseA, (lds_void_t*)(st + (8 * (wave + NW * q)) * 64), offA[q], 2 * k0);
             } else {
                 const int i = q - A_INS;
                 const int br0 = 8 * NW * i;
-                const char* bb = (NB == 2 && br0 >= BNH) ? bB1 : bB0;
-                __builtin_amdgcn_global_load_lds((gbl_void_t*)(bb + offB[i]),
-                                                 (lds_void_t*)(st + (BM + 8 * (wave + NW * i)) * 64), 16, 0, 0);
+                const char* bb = (NB == 2 && br0 >= BNH) ? baseB1 : baseB0;
+                buffer_load_lds16(bb, (lds_void_t*)(st + (BM + 8 * (wave + NW * i)) * 64), offB[i], 2 * k0);
             }
         }
     };
