@@ -184,10 +184,11 @@ moe_status moe_layer_forward(const moe_layer_desc *desc, const moe_weights *weig
                              void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /* As moe_layer_forward, and additionally records hipEvent_t events[i] (caller-created,
- * i = 0 .. MOE_NUM_STAGES, so MOE_NUM_STAGES + 1 events) on `stream` before the first stage
+ * i = 0 .. MOE_NUM_STAGES, so MOE_NUM_STAGES + 1 entries) on `stream` before the first stage
  * and after each stage, so that hipEventElapsedTime(events[i], events[i+1]) is stage i's
  * device time.  A stage that does not apply (capacity without a limit) has zero length.
- * events may be NULL (then this is moe_layer_forward). */
+ * A NULL entry records nothing at that boundary (to time one stage, pass only its two
+ * events); events may be NULL (then this is moe_layer_forward). */
 moe_status moe_layer_forward_timed(const moe_layer_desc *desc, const moe_weights *weights,
                                    const void *x, void *y, const moe_routing *routing,
                                    void *ws, size_t ws_bytes, moe_stream_t stream,

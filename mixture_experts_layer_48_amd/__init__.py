@@ -155,7 +155,8 @@ def moe_combine(desc, y_perm, inv, w, y, stream=None) -> None:
 
 def moe_layer_forward(desc, weights: Dict, x, y, routing: Optional[Dict] = None, ws=None, stream=None,
                       events: Optional[Sequence[int]] = None) -> None:
-    """The whole layer; `events` (MOE_NUM_STAGES + 1 hipEvent_t handles) selects the timed entry point."""
+    """The whole layer; `events` (MOE_NUM_STAGES + 1 hipEvent_t handles, None = no event at that
+    stage boundary) selects the timed entry point."""
     lib = load_library()
     wt = _weights(weights)
     r = moe_routing(*(_ptr((routing or {}).get(n)) for n in

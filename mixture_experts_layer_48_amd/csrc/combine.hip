@@ -4,7 +4,8 @@
 // plus the shared expert's output with weight 1 when the layer has one.
 //
 // One block per token; the fp32 expert rows are summed in slot order in fp32 and the result is
-// rounded once to the layer dtype, so the output does not depend on scheduling.
+// rounded once to the layer dtype, so the output does not depend on scheduling.  (bf16 layers
+// have d % 64 == 0, so every thread's 8 columns are whole.)
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -26,27 +27,47 @@ __device__ __forceinline__ void row8(const float* __restrict__ yp, long long par
     }
 }
 
-__global__ __launch_bounds__(256) void combine_bf16_kernel(const float* __restrict__ yp,
-                                                           const int32_t* __restrict__ inv,
-                                                           const float* __restrict__ w,
-                                                           bf16* __restrict__ y, int T, int k, int d,
-                                                           int has_shared, int nparts) {
+// One block per token, one thread per 8 columns (the block is as wide as d / 8 allows), so a
+// whole output row is one pass.  Slots are taken four at a time: their rows are loaded before
+// any of them is added, which keeps four rows' loads in flight, and the adds still run in slot
+// order.  A dropped slot (inv < 0) or a slot past k is neither loaded nor added.
+__global__ __launch_bounds__(1024) void combine_bf16_kernel(const float* __restrict__ yp,
+                                                            const int32_t* __restrict__ inv,
+                                                            const float* __restrict__ w,
+                                                            bf16* __restrict__ y, int T, int k, int d,
+                                                            int has_shared, int nparts) {
     const int t = blockIdx.x;
     const int32_t* iv = inv + (size_t)t * k;
     const float* wv = w ? w + (size_t)t * k : nullptr;
     const long long part_stride = ((long long)T * k + (has_shared ? T : 0)) * d;
     for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float v[8];
-        for (int j = 0; j < k; ++j) {
-            const int r = iv[j];
-            if (r < 0) continue;
-            const float s = wv ? wv[j] : 1.0f;
-            row8(yp, part_stride, nparts, (size_t)r * d + c, v);
+        for (int j0 = 0; j0 < k; j0 += 4) {
+            int r[4];
+            float sc[4];
+            bool ok[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(s, v[i], acc[i]);
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + q;
+                const int rr = j < k ? iv[j] : -1;
+                ok[q] = rr >= 0;
+                r[q] = rr;
+                sc[q] = (ok[q] && wv) ? wv[j] : 1.0f;
+            }
+            float v[4][8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (ok[q]) row8(yp, part_stride, nparts, (size_t)r[q] * d + c, v[q]);   // uniform per block
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (!ok[q]) continue;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(sc[q], v[q][i], acc[i]);
+            }
         }
         if (has_shared) {
+            float v[8];
             row8(yp, part_stride, nparts, ((size_t)T * k + t) * d + c, v);
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] += v[i];
@@ -81,9 +102,13 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
 hipError_t launch_combine(const void* y_perm, const int32_t* inv, const float* w, void* y, int T,
                           int k, int d, int has_shared, int dtype, int nparts, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (dtype == 1)
-        hipLaunchKernelGGL(combine_bf16_kernel, dim3(T), dim3(256), 0, s, (const float*)y_perm, inv, w,
+    if (dtype == 1) {
+        // one thread per 8 columns, in whole waves, at most 1024
+        int threads = ((d / 8 + 63) / 64) * 64;
+        threads = threads < 64 ? 64 : (threads > 1024 ? 1024 : threads);
+        hipLaunchKernelGGL(combine_bf16_kernel, dim3(T), dim3(threads), 0, s, (const float*)y_perm, inv, w,
                            (bf16*)y, T, k, d, has_shared, nparts < 1 ? 1 : nparts);
+    }
     else
         hipLaunchKernelGGL(combine_f32_kernel, dim3(T), dim3(256), 0, s, (const float*)y_perm, inv, w,
                            (float*)y, T, k, d, has_shared);

@@ -251,9 +251,6 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_weights
     if (st != MOE_OK) return st;
     if (d.T == 0) return MOE_OK;
     if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x and y are required");
-    if (events)
-        for (int i = 0; i <= MOE_NUM_STAGES; ++i)
-            if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events array holds a NULL event");
     const Layout L = layout_of(d);
     if (!ws || ws_bytes < L.total)
         return fail(MOE_ERR_WORKSPACE, "workspace too small for moe_layer_forward: need " + std::to_string(L.total));

@@ -118,8 +118,12 @@ def test_missing_pointers_and_small_workspace(lib):
     assert lib.moe_expert_ffn(ctypes.byref(desc), ctypes.byref(good), FAKE, FAKE, FAKE, None, FAKE, FAKE, 16,
                               None) == M.MOE_ERR_WORKSPACE
     assert lib.moe_combine(ctypes.byref(desc), None, FAKE, None, FAKE, None) == M.MOE_ERR_INVALID_ARG
-    events = (ctypes.c_void_p * (M.MOE_NUM_STAGES + 1))(*([FAKE] * M.MOE_NUM_STAGES + [None]))
+    # NULL entries in the events array are allowed (no event at that boundary); the timed entry
+    # point validates the rest like the plain one
+    events = (ctypes.c_void_p * (M.MOE_NUM_STAGES + 1))(*([None] * 3 + [FAKE, FAKE] + [None] * (M.MOE_NUM_STAGES - 4)))
     assert lib.moe_layer_forward_timed(ctypes.byref(desc), ctypes.byref(good), FAKE, FAKE, ctypes.byref(r), FAKE,
+                                       need - 1, None, events) == M.MOE_ERR_WORKSPACE
+    assert lib.moe_layer_forward_timed(ctypes.byref(desc), ctypes.byref(good), None, FAKE, ctypes.byref(r), FAKE,
                                        need, None, events) == M.MOE_ERR_INVALID_ARG
 
 
