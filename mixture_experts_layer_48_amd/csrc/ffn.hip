@@ -364,13 +364,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
 // For a few rows per expert the GEMMs are weight streams: every weight byte of a touched expert
 // is read once and used for at most 16 rows.  One wave owns one 16-column group of one segment
 // and the whole K range; its B fragments (16 weight rows x 32 K for v_mfma_f32_16x16x32_bf16)
-// come straight from memory into registers, several steps ahead, and its A fragments (the <= 16
-// rows, gathered through perm for the in-projection) are shared by all waves through L2.  Empty
-// experts are skipped, so only touched experts' weights are read.  Segments with more than 16
-// rows loop over 16-row tiles.
-#define SK_UNROLL 8
-
-template <int MODE>
+// come straight from memory into registers, U steps at a time, and its A fragments (the <= 16
+// rows, gathered through perm for the in-projection) are shared by all waves through L2.  Waves
+// are numbered segment, then column group, so the waves of a block stream neighbouring weight
+// rows.  Empty experts are skipped, so only touched
+// experts' weights are read.  Segments with more than 16 rows loop over 16-row tiles.  (Weight
+// loads stay cached: a load instruction covers half of each 128-byte line it touches and the
+// next K step reads the other half; non-temporal loads measured slower.)
+template <int MODE, int U>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
     constexpr int NB = (MODE == MODE_IN_SWIGLU) ? 2 : 1;
     const int lane = threadIdx.x & 63;
@@ -394,12 +395,12 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
         if (NB == 2) B1 = a.S1;
     }
     if (row_end <= row_beg) return;                             // expert not touched
+    const int KS = a.K / 32;
     const int col = cg * 16 + (lane & 15);                      // this lane's B column
     const int colc = col < a.Ncols ? col : a.Ncols - 1;
     const int kq = (lane >> 4) * 8;                             // this lane's K offset in a step
     const bf16* pb0 = B0 + (size_t)colc * a.K + kq;
     const bf16* pb1 = (NB == 2) ? B1 + (size_t)colc * a.K + kq : nullptr;
-    const int KS = a.K / 32;
     for (int m0 = row_beg; m0 < row_end; m0 += 16) {
         const int r = m0 + (lane & 15);                         // this lane's A row
         const bool rok = r < row_end;
@@ -410,16 +411,16 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         const bf16x8 zero8 = {};
         int ks = 0;
-        for (; ks + SK_UNROLL <= KS; ks += SK_UNROLL) {
-            bf16x8 b0[SK_UNROLL], b1[SK_UNROLL], av[SK_UNROLL];
+        for (; ks + U <= KS; ks += U) {
+            bf16x8 b0[U], b1[U], av[U];
 #pragma unroll
-            for (int u = 0; u < SK_UNROLL; ++u) {
+            for (int u = 0; u < U; ++u) {
                 b0[u] = *(const bf16x8*)(pb0 + (ks + u) * 32);
                 if (NB == 2) b1[u] = *(const bf16x8*)(pb1 + (ks + u) * 32);
                 av[u] = rok ? *(const bf16x8*)(pa + (ks + u) * 32) : zero8;
             }
 #pragma unroll
-            for (int u = 0; u < SK_UNROLL; ++u) {
+            for (int u = 0; u < U; ++u) {
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b0[u], acc0, 0, 0, 0);
                 if (NB == 2) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b1[u], acc1, 0, 0, 0);
             }
@@ -452,14 +453,19 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
     }
 }
 
-template <int MODE>
+template <int MODE, int U>
 static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
     const long long waves = (long long)(a.N + (a.has_shared ? 1 : 0)) * ((a.Ncols + 15) / 16);
-    hipLaunchKernelGGL(ffn_skinny_kernel<MODE>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+    auto kern = ffn_skinny_kernel<MODE, U>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 // Decode-sized batches (at most 16 rows per expert on average) take the weight-streaming path.
+// Unroll depths: the in-projection's shallower unroll keeps its registers low enough that all of
+// its waves are resident at once.
+#define SK_U_IN 4
+#define SK_U_OUT 8
 static bool skinny(const FfnLaunch& f) { return (long long)f.T * f.k <= 16LL * f.N; }
 
 // ------------------------------------------------------------------ fp32 path
@@ -538,8 +544,10 @@ static bool big_tiles(const FfnLaunch& f) {
 // last round of blocks on the CUs mostly empty.  The parts' fp32 outputs are summed, in order,
 // by the combine.
 int ffn_out_ksplit(int T, int k, int N, int d, int d_ff, int has_shared, int dtype) {
-    if (dtype != 1 || d_ff % (2 * FB_BK) != 0 || d_ff < 8192) return 1;
+    if (dtype != 1) return 1;
     const long long rows = (long long)T * k;
+    if (rows <= 16LL * N) return 1;                        // weight streaming (decode)
+    if (d_ff % (2 * FB_BK) != 0 || d_ff < 8192) return 1;
     if (rows < 192LL * N) return 1;                       // small-tile path: many blocks already
     const long long tiles = ((rows + 255) / 256 + N + (has_shared ? (T + 255) / 256 : 0)) * ((d + 255) / 256);
     return tiles < 4 * 256 ? 2 : 1;
@@ -559,13 +567,13 @@ hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
         if (f.ffn == 1) {
             a.B0 = (const bf16*)f.w_gate; a.B1 = (const bf16*)f.w_up;
             a.S0 = (const bf16*)f.sh_gate; a.S1 = (const bf16*)f.sh_up;
-            if (skinny(f)) return launch_skinny<MODE_IN_SWIGLU>(a, s);
+            if (skinny(f)) return launch_skinny<MODE_IN_SWIGLU, SK_U_IN>(a, s);
             if (big_tiles(f)) return launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, s);
             return launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, s);
         }
         a.B0 = (const bf16*)f.w_up;
         a.S0 = (const bf16*)f.sh_up;
-        if (skinny(f)) return launch_skinny<MODE_IN_RELU>(a, s);
+        if (skinny(f)) return launch_skinny<MODE_IN_RELU, SK_U_IN>(a, s);
         if (big_tiles(f)) return launch_bf16<MODE_IN_RELU, 256, 256, 2, 2>(a, s);
         return launch_bf16<MODE_IN_RELU, 128, 128, 2, 2>(a, s);
     }
@@ -597,7 +605,7 @@ hipError_t launch_ffn_out(const FfnLaunch& f, hipStream_t s) {
         a.K = f.d_ff; a.Ncols = f.d;
         a.ksplit = f.ksplit;
         a.part_stride = (long long)((long long)f.T * f.k + (f.has_shared ? f.T : 0)) * f.d;
-        if (skinny(f)) return launch_skinny<MODE_OUT>(a, s);
+        if (skinny(f)) return launch_skinny<MODE_OUT, SK_U_OUT>(a, s);
         if (big_tiles(f)) return launch_bf16<MODE_OUT, 256, 256, 2, 2>(a, s);
         return launch_bf16<MODE_OUT, 128, 128, 2, 2>(a, s);
     }

@@ -44,14 +44,15 @@ def _desc(**kw):
 
 
 def test_workspace_size_grows_with_tokens_and_is_zero_when_invalid():
-    a = M.moe_workspace_size(_desc(T=64))
-    b = M.moe_workspace_size(_desc(T=128))
+    # both above the decode regime (> 16 routed rows per expert)
+    a = M.moe_workspace_size(_desc(T=128))
+    b = M.moe_workspace_size(_desc(T=256))
     assert 0 < a < b
     assert M.moe_workspace_size(_desc(k=9)) == 0
     # hidden state and per-row outputs dominate: (T*k rows) x (d_ff + d) x 2 bytes at least
-    assert a >= 64 * 2 * (256 + 128) * 2
-    cap = M.moe_workspace_size(_desc(capacity_factor=2.0))
-    assert cap >= a + 64 * 8            # ranked expert lists
+    assert a >= 128 * 2 * (256 + 128) * 2
+    cap = M.moe_workspace_size(_desc(T=128, capacity_factor=2.0))
+    assert cap >= a + 128 * 8           # ranked expert lists
 
 
 FAKE = 0x1000   # never dereferenced: every call below fails validation on the host
