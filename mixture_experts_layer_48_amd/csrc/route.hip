@@ -270,23 +270,24 @@ __global__ __launch_bounds__(64) void rank_sort_kernel(const float* __restrict__
 // down, so a token never returns to an expert that turned it away, and the fixed point is the
 // token-by-token first-come assignment.
 //
-// The chunk's ranked lists sit in LDS (4 ranks per dword, rank-major, so a wave's lanes read
-// neighbouring words); "room at chunk start" and "already held" are bits in registers, so a
-// token steps over full experts without touching memory.  Proposal counts are per wave, stamped
-// with the round number, so no round has to clear them.
+// A 64-rank window of each chunk token's ranked list sits in LDS (4 ranks per dword,
+// rank-major, so a wave's lanes read neighbouring words), starting at the 16-rank boundary at
+// or before the rank the token resumes from; picks are shallow (on the skewed layer every pick
+// is within 41 ranks), and a scan that runs past the window reads the list from memory.  The
+// window keeps a chunk at one token per thread.  "Room at chunk start" is a byte table in LDS
+// and "already held" is in registers, so a token steps over full experts cheaply.  Proposal
+// counts are per wave, stamped with the round number, so no round has to clear them.
 #define CAP_THREADS 1024
-#define CAP_WAVES (CAP_THREADS / 64)
-#define CAP_RK_WORDS 24576          // 96 KiB of ranked lists per chunk
+#define CAP_WIN 4                   // 16-byte pieces (16 ranks each) in a token's window
 
-// NVMAX: 16-byte pieces of a ranked row kept in registers (8: N <= 128, 16: N <= 256); THREADS:
-// block size (1024, or 512 so that the 16 pieces fit the register budget).
-template <int NVMAX, int THREADS>
+template <int THREADS>
 __global__ __launch_bounds__(THREADS) void capacity_kernel(
     const uint8_t* __restrict__ ranked, uint8_t* __restrict__ rpos, int T, int N, int NP, int CT, int k,
     int C, int32_t* __restrict__ idx) {
     constexpr int CAP_THREADS_ = THREADS;
     constexpr int CAP_WAVES_ = THREADS / 64;
-    __shared__ uint32_t rk4[CAP_RK_WORDS];              // [NP / 4][CT]
+    constexpr int WW = 4 * CAP_WIN;                     // window words
+    __shared__ uint32_t rk4[WW * THREADS];              // [WW][CT]
     __shared__ uint32_t cnt[CAP_WAVES_][MOE_MAX_EXPERTS]; // (round << 16) | proposals of the wave
     __shared__ int fill[MOE_MAX_EXPERTS];
     __shared__ int tau[MOE_MAX_EXPERTS];
@@ -295,26 +296,29 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
     (void)lane;
     const int wave = tid >> 6;
     const int NQ = NP >> 2;               // words per ranked row (multiple of 4)
-    const int NV = NQ >> 2;               // 16-byte pieces per ranked row (<= 16)
     for (int e = tid; e < MOE_MAX_EXPERTS; e += CAP_THREADS_) fill[e] = 0;
     for (int i = tid; i < CAP_WAVES_ * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&cnt[0][0])[i] = 0u;
     uint32_t round = 0;                   // stamps of cnt; never reused without clearing
 
-    // next chunk's state of this thread's token, fetched during the current chunk: its ranked
-    // row, the first four experts it already holds and the rank after its previous slot's pick
-    u32x4 pre[NVMAX];
-    int ph0 = -1, ph1 = -1, ph2 = -1, ph3 = -1, pstart = 0;
+    // next chunk's state of this thread's token, fetched during the current chunk: the window
+    // of its ranked row, the first four experts it already holds and the rank after its
+    // previous slot's pick
+    u32x4 pre[CAP_WIN];
+    int ph0 = -1, ph1 = -1, ph2 = -1, ph3 = -1, pstart = 0, pq0 = 0;
     auto prefetch = [&](int t_next, int j_next) {
         if (tid >= CT || t_next >= T) return;
-#pragma unroll
-        for (int i = 0; i < NVMAX; ++i)
-            if (i < NV) pre[i] = ((const u32x4*)(ranked + (size_t)t_next * NP))[i];
         const int32_t* ir = idx + (size_t)t_next * k;
         ph0 = j_next > 0 ? ir[0] : -1;
         ph1 = j_next > 1 ? ir[1] : -1;
         ph2 = j_next > 2 ? ir[2] : -1;
         ph3 = j_next > 3 ? ir[3] : -1;
         pstart = j_next > 0 ? rpos[t_next] : 0;
+        pq0 = (pstart >> 4) << 2;                           // window start (words), 16-rank aligned
+        const u32x4* row = (const u32x4*)(ranked + (size_t)t_next * NP) + (pq0 >> 2);
+        const int npieces = (NQ - pq0) >> 2;                // pieces left in the row
+#pragma unroll
+        for (int i = 0; i < CAP_WIN; ++i)
+            if (i < npieces) pre[i] = row[i];
     };
     const int nchunks = (T + CT - 1) / CT;
     prefetch(tid, 0);
@@ -325,10 +329,12 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
             const int c0 = ci * CT;
             const int t = c0 + tid;
             const bool active = tid < CT && t < T;
+            const int wq0 = pq0;                            // this chunk token's window start
             if (active) {
+                const int npieces = (NQ - wq0) >> 2;
 #pragma unroll
-                for (int i = 0; i < NVMAX; ++i)
-                    if (i < NV) {
+                for (int i = 0; i < CAP_WIN; ++i)
+                    if (i < npieces) {
                         rk4[(4 * i + 0) * CT + tid] = pre[i][0];
                         rk4[(4 * i + 1) * CT + tid] = pre[i][1];
                         rk4[(4 * i + 2) * CT + tid] = pre[i][2];
@@ -354,7 +360,9 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                 if (choose) {                             // next candidate from (q, bpos) on
                     choice = -1;
                     while (q < NQ) {
-                        const uint32_t wd = rk4[q * CT + tid];
+                        const int wi = q - wq0;             // >= 0: the scan starts in the window
+                        const uint32_t wd = wi < WW ? rk4[wi * CT + tid]
+                                                    : *(const uint32_t*)(ranked + (size_t)t * NP + 4 * q);
                         // room flags of the word's four experts, one bit each
                         const uint32_t rf = (uint32_t)roomb[wd & 0xFF] | ((uint32_t)roomb[(wd >> 8) & 0xFF] << 1) |
                                             ((uint32_t)roomb[(wd >> 16) & 0xFF] << 2) |
@@ -499,17 +507,11 @@ hipError_t launch_capacity(const float* z, uint8_t* ranked, int T, int N, int k,
     hipLaunchKernelGGL(rank_sort_kernel, dim3(T), dim3(64), 0, s, z, T, N, NP, ranked);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // tokens per chunk: as many as the 96 KiB ranked-list buffer holds, a multiple of 64, at most
-    // one per thread
-    const int threads = NP <= 128 ? 1024 : 512;
-    int CT = (CAP_RK_WORDS / (NP / 4)) & ~63;
-    CT = CT > threads ? threads : CT;
-    if (NP <= 128)
-        hipLaunchKernelGGL((capacity_kernel<8, 1024>), dim3(1), dim3(1024), 0, s, ranked, ranked + (size_t)T * NP,
-                           T, N, NP, CT, k, C, idx);
-    else
-        hipLaunchKernelGGL((capacity_kernel<16, 512>), dim3(1), dim3(512), 0, s, ranked, ranked + (size_t)T * NP,
-                           T, N, NP, CT, k, C, idx);
+    // one token per thread and chunk (the ranked-list windows of 1024 tokens take 64 KiB of LDS)
+    const int CT = CAP_THREADS;
+    auto kern = capacity_kernel<CAP_THREADS>;
+    hipLaunchKernelGGL(kern, dim3(1), dim3(CAP_THREADS), 0, s, ranked, ranked + (size_t)T * NP, T, N, NP, CT,
+                       k, C, idx);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(slot_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, z, idx, T, N, k, gating, w);
