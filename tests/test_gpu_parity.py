@@ -66,6 +66,14 @@ SMALL = {
                                         ffn=W.FFN_RELU2, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=22),
     "tiles256_ragged_cols": W.LayerConfig("tiles256_ragged_cols", T=300, d=256, N=1, k=1, d_ff=448, dtype="bf16",
                                         ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=23),
+    # capacity with 256 experts: scans that run past the ranked-list window kept in LDS (picks
+    # deeper than 64 ranks), with slots dropped once every expert is full, and without drops
+    "capacity_deep_drops": W.LayerConfig("capacity_deep_drops", T=300, d=64, N=256, k=2, d_ff=64, dtype="bf16",
+                                         ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, capacity_factor=0.5,
+                                         zipf_bias=True, seed=24),
+    "capacity_deep_n256": W.LayerConfig("capacity_deep_n256", T=2000, d=64, N=256, k=2, d_ff=64, dtype="bf16",
+                                        ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, capacity_factor=1.0,
+                                        zipf_bias=True, seed=25),
     # at most 16 routed rows per expert on average: the weight-streaming decode GEMMs, here with a
     # shared expert longer than one 16-row tile, heavy experts, and capacity drops
     "skinny_relu_shared": W.LayerConfig("skinny_relu_shared", T=24, d=128, N=16, k=2, d_ff=192, dtype="bf16",
