@@ -252,10 +252,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
             if (i < n_ld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
         }
     };
-    auto issue_part = [&](bf16* st, int k0, int beg, int end) {
+    // A variant with NV sub-tiles per wave reads rows [0, NV * WGM * 32) of the A tile only, so
+    // its direct loads skip the rest (those LDS rows are never read).
+    auto issue_part = [&](bf16* st, int k0, int beg, int end, auto nv) {
+        constexpr int A_NEED = decltype(nv)::value * WGM * 32 / (8 * NW);
 #pragma unroll
         for (int q = 0; q < NLD; ++q) {
             if (q < beg || q >= end) continue;
+            if (q < A_INS && q >= A_NEED) continue;
             if (q < A_INS) {
                 buffer_load_lds16(baseA, (lds_void_t*)(st + (8 * (wave + NW * q)) * 64), offA[q], 2 * k0);
             } else {
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     auto stage = [&](Acc& acc, bf16* cur, bf16* nxt, int k_next, int k_after, Frags& f0, Frags& f1, auto nv) {
         constexpr int NDS = decltype(nv)::value + NB * TN;   // fragment reads per K=16 step
         load_frags(cur, 1, f1, nv);
-        issue_part(nxt, k_next, NLD0, NLD);
+        issue_part(nxt, k_next, NLD0, NLD, nv);
         mfmas(acc, f0, nv);
         interleave(NDS, NLD - NLD0, nv);
         __builtin_amdgcn_sched_barrier(0);
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0070);    // vmcnt(0) lgkmcnt(0): own loads and reads done
         __syncthreads();                       // next stage visible; this stage no longer read
         load_frags(nxt, 0, f0, nv);
-        issue_part(cur, k_after, 0, NLD0);
+        issue_part(cur, k_after, 0, NLD0, nv);
         mfmas(acc, f1, nv);
         interleave(NDS, NLD0, nv);
         __builtin_amdgcn_sched_barrier(0);
@@ -340,12 +344,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         float sc = 1.0f;
         if (MODE == MODE_OUT && tid < BM && m0 + tid < row_end && a.row_scale && seg < a.N)
             sc = a.row_scale[a.perm[m0 + tid]];
-        issue_part(st0, kbase, 0, NLD);
+        issue_part(st0, kbase, 0, NLD, nv);
         __builtin_amdgcn_s_waitcnt(0x0070);
         if (MODE == MODE_OUT && tid < BM) s_scale[tid] = sc;
         __syncthreads();
         load_frags(st0, 0, fa, nv);
-        issue_part(st1, kofs(1), 0, NLD0);
+        issue_part(st1, kofs(1), 0, NLD0, nv);
         int kt = 0;
         for (; kt + 2 <= KT; kt += 2) {
             stage(acc, st0, st1, kofs(kt + 1), kofs(kt + 2), fa, fb, nv);
