@@ -74,28 +74,37 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, lds_void_t* 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
 
-// Work split, computed by wave 0 of every block.  From offsets it counts the real m-tiles of
-// each segment (ceil(rows / BM)); the real tiles are numbered segment by segment.  Within a
-// segment they go in rectangles of at most 8 m-tiles x (32 / that) n-tiles, m fastest inside a
-// rectangle: 32 blocks are what one XCD runs at once (32 CUs, one block each), so the blocks
-// that run together on an XCD cover a compact rectangle and share its row tiles and weight
-// tiles in that XCD's L2 (a column of 32 m-tiles against one n-tile would fetch every row tile
-// again for every n-tile).  The 8 XCDs get equal contiguous ranges of the numbering; blocks are
-// dealt to XCDs round-robin (block b runs on XCD b % 8 as its (b / 8)-th block), so every XCD
-// gets the same amount of real work.  s_info receives segment (-1: no tile), m-tile, n-tile and
-// K part.
+// Work split.  Wave 0 of every block turns offsets into a segment table in LDS: each segment's
+// first tile, its m-tile count (ceil(rows / BM)) and its row range.  Real tiles are numbered
+// segment by segment, K part outermost.  Within a segment they go in rectangles of at most 8
+// m-tiles x (32 / that) n-tiles, m fastest inside a rectangle: one XCD works on 32 tiles at once
+// (32 CUs, one block each), so the tiles it holds together cover a compact rectangle and share
+// its row tiles and weight tiles in that XCD's L2 (a column of 32 m-tiles against one n-tile
+// would fetch every row tile again for every n-tile).  The 8 XCDs get equal contiguous ranges
+// of the numbering (block b runs on XCD b % 8).
+//
+// The kernel is persistent: the grid holds only as many blocks as the CUs keep resident, and
+// each block runs a sequence of tiles.  Within an XCD's range, round i of tiles goes to the
+// XCD's blocks in order, reversed on odd rounds, so that a pattern of period two (a full m-tile
+// next to an expert's short last one) does not fall on the same blocks every round.
+#define FFN_MAX_SEG 320   // 5 segments per lane of one wave: routed experts and the shared one
+
 template <int BM>
-__device__ __forceinline__ void decode_tile(const FfnKArgs& a, int lane, int* s_info) {
-    const int b = blockIdx.x;
-    const int xcd = b & 7, j = b >> 3;
-    int tl[5], loc = 0;
+__device__ __forceinline__ void build_segments(const FfnKArgs& a, int lane, int* s_tab, int* s_R1) {
+    int tl[5], beg[5], rows[5], loc = 0;
 #pragma unroll
     for (int q = 0; q < 5; ++q) {
         const int s = lane * 5 + q;
-        int rows = 0;
-        if (s < a.N) rows = a.offsets[s + 1] - a.offsets[s];
-        else if (s == a.N && a.has_shared) rows = a.T;
-        tl[q] = (rows + BM - 1) / BM;
+        beg[q] = 0;
+        rows[q] = 0;
+        if (s < a.N) {
+            beg[q] = a.offsets[s];
+            rows[q] = a.offsets[s + 1] - beg[q];
+        } else if (s == a.N && a.has_shared) {
+            beg[q] = a.T * a.k;
+            rows[q] = a.T;
+        }
+        tl[q] = (rows[q] + BM - 1) / BM;
         loc += tl[q];
     }
     int incl = loc;
@@ -104,34 +113,69 @@ __device__ __forceinline__ void decode_tile(const FfnKArgs& a, int lane, int* s_
         const int v = __shfl_up(incl, o, 64);
         if (lane >= o) incl += v;
     }
-    const int R1 = __shfl(incl, 63, 64) * a.n_tiles;   // tiles of one K part
-    const int R = R1 * a.ksplit;
-    const int per_xcd = (R + 7) / 8;
-    int t = (j < per_xcd) ? xcd * per_xcd + j : R;     // tile id, R = none
-    const int ks = t < R ? t / R1 : 0;                  // K part (outermost)
-    if (t < R) t -= ks * R1;
-    else t = R1;
-    int run = (incl - loc) * a.n_tiles;
+    int run = incl - loc;
 #pragma unroll
     for (int q = 0; q < 5; ++q) {
-        const int cnt = tl[q] * a.n_tiles;
-        if (t >= run && t < run + cnt) {
-            const int rem = t - run, tm = tl[q];
-            const int GM = tm < 8 ? tm : 8;               // m-tiles per rectangle
-            const int GN = 32 / GM;                       // n-tiles per rectangle
-            const int mg = rem / (GM * a.n_tiles);        // rectangle row (GM m-tiles, all n)
-            const int gm = min(GM, tm - mg * GM);         // m-tiles in this row (last may be short)
-            const int r2 = rem - mg * GM * a.n_tiles;
-            const int band = r2 / (gm * GN);              // rectangle within the row
-            const int r3 = r2 - band * gm * GN;
-            s_info[0] = lane * 5 + q;
-            s_info[1] = mg * GM + r3 % gm;
-            s_info[2] = band * GN + r3 / gm;
-        }
-        run += cnt;
+        const int s = lane * 5 + q;
+        s_tab[s] = run * a.n_tiles;
+        s_tab[FFN_MAX_SEG + s] = tl[q];
+        s_tab[2 * FFN_MAX_SEG + s] = beg[q];
+        s_tab[3 * FFN_MAX_SEG + s] = beg[q] + rows[q];
+        run += tl[q];
     }
-    if (lane == 63 && t >= R1) s_info[0] = -1;
-    if (lane == 0) s_info[3] = ks;
+    if (lane == 63) *s_R1 = incl * a.n_tiles;
+}
+
+// Two floats rounded to bf16 (nearest even, as a bf16 conversion) in one 32-bit word, the
+// first in the low half.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// A pointer every lane holds the same value of, kept in scalar registers (a buffer descriptor
+// must be uniform).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+    const unsigned long long v = (unsigned long long)p;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+    return (const char*)(((unsigned long long)hi << 32) | lo);
+}
+
+struct TileInfo {
+    int seg, mt, nt, kpart, row_beg, row_end;
+};
+
+// Tile t (0 <= t < R1 * ksplit) -> segment, m-tile, n-tile and K part, one tile per lane.  The
+// segment is found by a binary search for the last one whose first tile is <= t (an empty
+// segment starts where the next one does, so the last of equal starts is the one holding t).
+__device__ __forceinline__ TileInfo decode_lane(const FfnKArgs& a, const int* s_tab, int R1, int t) {
+    TileInfo ti;
+    ti.kpart = t / R1;
+    const int tt = t - ti.kpart * R1;
+    int lo = 0, hi = a.N + (a.has_shared ? 1 : 0) - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tab[mid] <= tt) lo = mid;
+        else hi = mid - 1;
+    }
+    ti.seg = lo;
+    const int tm = s_tab[FFN_MAX_SEG + lo];
+    const int rem = tt - s_tab[lo];
+    const int GM = tm < 8 ? tm : 8;
+    const int GN = 32 / GM;
+    const int mg = rem / (GM * a.n_tiles);
+    const int gm = min(GM, tm - mg * GM);
+    const int r2 = rem - mg * GM * a.n_tiles;
+    const int band = r2 / (gm * GN);
+    const int r3 = r2 - band * gm * GN;
+    ti.mt = mg * GM + r3 % gm;
+    ti.nt = band * GN + r3 / gm;
+    ti.row_beg = s_tab[2 * FFN_MAX_SEG + lo];
+    ti.row_end = s_tab[3 * FFN_MAX_SEG + lo];
+    return ti;
 }
 
 template <int MODE, int BM, int BNH, int WGM, int WGN>
@@ -143,65 +187,112 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     constexpr int A_INS = BM / (8 * NW);             // load instructions per wave per stage (A)
     constexpr int B_INS = Cfg::BROWS / (8 * NW);     // (B)
     static_assert(BM % (8 * NW) == 0 && Cfg::BROWS % (8 * NW) == 0, "load split");
+    static_assert(BM <= 64 * NW, "one thread per row of the A tile");
     // two stages in two distinct LDS objects, so the compiler can tell a fragment read of one
     // stage from the asynchronous loads into the other
     __shared__ __attribute__((aligned(1024))) bf16 st0[ROWS * 64];
     __shared__ __attribute__((aligned(1024))) bf16 st1[ROWS * 64];
-    __shared__ int s_info[4];
-    __shared__ float s_scale[MODE == MODE_OUT ? BM : 1];   // gate weight of each row of the tile
+    __shared__ int s_tab[4 * FFN_MAX_SEG];
+    __shared__ int s_R1;
+    __shared__ int s_tiles[64 * 6];                            // this block's next 64 tiles
+    __shared__ int s_src[MODE == MODE_OUT ? 1 : BM];          // next tile's x row of each A row
+    __shared__ float s_scale[MODE == MODE_OUT ? 2 * BM : 1];  // gate weight of each row, 2 tiles
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go to M0
-    if (wave == 0) decode_tile<BM>(a, lane, s_info);
+    if (wave == 0) build_segments<BM>(a, lane, s_tab, &s_R1);
     __syncthreads();
-    const int seg = s_info[0];
-    if (seg < 0) return;
-    const int mt = s_info[1];
-    const int n_tile = s_info[2];
-    const int kpart = s_info[3];
+    const int R1 = __builtin_amdgcn_readfirstlane(s_R1);
+    const int R = R1 * a.ksplit;
+    const int nbx = gridDim.x >> 3, xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
+    const int per = (R + 7) >> 3, lo = xcd * per, hi = min(R, lo + per);
+    auto tile_id = [&](int i) { return lo + i * nbx + ((i & 1) ? nbx - 1 - jb : jb); };
+    int it = 0;                                          // tiles done by this block
+    if (tile_id(0) >= hi) return;
+    // wave 0 decodes this block's tiles 64 at a time, one per lane, into s_tiles
+    auto decode_chunk = [&](int c) {
+        const int t = tile_id(c * 64 + lane);
+        if (t < hi) {
+            const TileInfo ti = decode_lane(a, s_tab, R1, t);
+            int* p = s_tiles + lane * 6;
+            p[0] = ti.seg; p[1] = ti.mt; p[2] = ti.nt; p[3] = ti.kpart; p[4] = ti.row_beg; p[5] = ti.row_end;
+        }
+    };
+    auto read_tile = [&](int i) {
+        const int* p = s_tiles + (i & 63) * 6;
+        TileInfo ti;
+        ti.seg = __builtin_amdgcn_readfirstlane(p[0]);
+        ti.mt = __builtin_amdgcn_readfirstlane(p[1]);
+        ti.nt = __builtin_amdgcn_readfirstlane(p[2]);
+        ti.kpart = __builtin_amdgcn_readfirstlane(p[3]);
+        ti.row_beg = __builtin_amdgcn_readfirstlane(p[4]);
+        ti.row_end = __builtin_amdgcn_readfirstlane(p[5]);
+        return ti;
+    };
+    if (wave == 0) decode_chunk(0);
+    __syncthreads();
+    TileInfo cur = read_tile(0);
+
+    const int KT = a.K / FB_BK / a.ksplit;               // stages of one tile
+    // A tile's last two stages load the next tile's first stage (and half of its second) into
+    // the LDS slots they free, when the next tile starts in slot 0 (an even stage count).
+    const bool chain = (KT % 2 == 0) && KT >= 4;
     const size_t wstride = (size_t)a.Ncols * a.K;
-    int row_beg, row_end;
-    const bf16 *B0, *B1 = nullptr;
-    if (seg < a.N) {
-        row_beg = a.offsets[seg];
-        row_end = a.offsets[seg + 1];
-        B0 = a.B0 + seg * wstride;
-        if (NB == 2) B1 = a.B1 + seg * wstride;
-    } else {
-        row_beg = a.T * a.k;
-        row_end = row_beg + a.T;
-        B0 = a.S0;
-        if (NB == 2) B1 = a.S1;
-    }
-    const int m0 = row_beg + mt * BM;
-    const int n0 = n_tile * BNH;
+    const char* baseA = (const char*)a.A;
 
     // per-lane 32-bit byte offsets of this wave's load instructions from a uniform base
     // (x / H stay below 4 GiB, one expert's weight matrix too)
     const int lrow = lane >> 3;                          // row within the 8-row group
-    // element offset of the chunk lane fetches for LDS row group g (8 rows)
-    auto lchunk = [&](int g) { return ((lane & 7) ^ ((4 * g + (lane >> 4)) & 7)) * 8; };
-    uint32_t offA[A_INS];
+    // Lane-derived values are recomputed where a tile's offsets are set (an empty asm hides the
+    // lane id from the optimiser there), instead of being precomputed once per row group and
+    // held in registers for the whole kernel.
+    auto fresh_lane = [&]() {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        return l;
+    };
+    // element offset of the chunk lane fetches for LDS row group g (8 rows): ((lane & 7) ^
+    // ((4g + (lane >> 4)) & 7)) * 8.  Every group this wave loads (A: g = wave + NW*i, B: g =
+    // BM/8 + wave + NW*i) has 4g = 4*wave (mod 8), so one value serves all of its loads.
+    static_assert((4 * NW) % 8 == 0 && (4 * (BM / 8)) % 8 == 0, "one chunk offset per lane");
+    auto a_row = [&](const TileInfo& ti, int i, int l) {  // row of A load i (rows past the end: row 0)
+        const int m0 = ti.row_beg + ti.mt * BM, rl = 8 * (wave + NW * i) + (l >> 3);
+        return (m0 + rl < ti.row_end) ? m0 + rl : m0;
+    };
+    auto a_src = [&](const TileInfo& ti, int r) {        // x row of slot row r (in-projection)
+        if (MODE == MODE_OUT) return r;
+        return (ti.seg < a.N) ? a.perm[r] / a.k : r - a.T * a.k;
+    };
+    uint32_t offA[A_INS], offB[B_INS];
+    const char *baseB0, *baseB1;
+    auto set_b = [&](const TileInfo& ti) {
+        const int n0 = ti.nt * BNH;
+        const int l = fresh_lane();
+        const uint32_t lc = (uint32_t)(((l & 7) ^ ((4 * wave + (l >> 4)) & 7)) * 8);
 #pragma unroll
-    for (int i = 0; i < A_INS; ++i) {
-        const int rl = 8 * (wave + NW * i) + lrow;
-        const int r = (m0 + rl < row_end) ? m0 + rl : m0;
-        int src;
-        if (MODE == MODE_OUT) src = r;
-        else src = (seg < a.N) ? a.perm[r] / a.k : r - a.T * a.k;
-        offA[i] = ((uint32_t)src * (uint32_t)a.K + (uint32_t)lchunk(wave + NW * i)) * 2u;
-    }
-    uint32_t offB[B_INS];
+        for (int i = 0; i < B_INS; ++i) {
+            const int br = 8 * (wave + NW * i) + (l >> 3);   // row of the B tile
+            const int n = n0 + (br % BNH);
+            const int nc = n < a.Ncols ? n : n0;
+            offB[i] = ((uint32_t)nc * (uint32_t)a.K + lc) * 2u;
+        }
+        const bf16* B0 = (ti.seg < a.N) ? a.B0 + ti.seg * wstride : a.S0;
+        const bf16* B1 = (NB == 2) ? ((ti.seg < a.N) ? a.B1 + ti.seg * wstride : a.S1) : B0;
+        baseB0 = uniform_ptr((const char*)B0);
+        baseB1 = uniform_ptr((const char*)B1);
+    };
+    auto set_a_direct = [&](const TileInfo& ti) {
+        const int l = fresh_lane();
+        const uint32_t lc = (uint32_t)(((l & 7) ^ ((4 * wave + (l >> 4)) & 7)) * 8);
 #pragma unroll
-    for (int i = 0; i < B_INS; ++i) {
-        const int br = 8 * (wave + NW * i) + lrow;       // row of the B tile
-        const int n = n0 + (br % BNH);
-        const int nc = n < a.Ncols ? n : n0;
-        offB[i] = ((uint32_t)nc * (uint32_t)a.K + (uint32_t)lchunk((BM >> 3) + wave + NW * i)) * 2u;
-    }
-    const char* baseA = (const char*)a.A;
-    const char* baseB0 = (const char*)B0;
-    const char* baseB1 = (const char*)(NB == 2 ? B1 : B0);
+        for (int i = 0; i < A_INS; ++i)
+            offA[i] = ((uint32_t)a_src(ti, a_row(ti, i, l)) * (uint32_t)a.K + lc) * 2u;
+    };
+    auto scale_of = [&](const TileInfo& ti) {            // gate weight of this thread's row
+        const int r = ti.row_beg + ti.mt * BM + tid;
+        return (tid < BM && r < ti.row_end && a.row_scale && ti.seg < a.N) ? a.row_scale[a.perm[r]] : 1.0f;
+    };
+
     const int wm = wave / WGN, wn = wave % WGN;
     // fragment addresses: rows of one wave's fragments differ by multiples of 32, so their
     // swizzle only depends on the lane: row r, chunk c sits at r*64 + ((c ^ ((r >> 1) & 7)) << 3)
@@ -220,27 +311,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
             for (int j = 0; j < TN; ++j)
                 f.b[m][j] = *(const bf16x8*)(st + bbase + (m * BNH + j * 32) * 64 + xo);
     };
-    // The tile's 32-row sub-tiles are dealt to the wave rows in turn (sub-tile s to wave row
-    // s % WGM), so the rows of a short tile (an expert's last one) spread over all waves.  A tile
-    // whose valid sub-tiles fit in NV per wave runs the variant with NV sub-tiles per wave and
-    // skips the MFMAs and fragment reads of the rest; rows past the end were loaded as copies of
-    // the first row and are never stored.
-    const int rows_valid = row_end - m0;
-    const int nsub = (rows_valid + 31) / 32;
+    // The weight fragment is the MFMA's first operand and the row fragment its second, so each
+    // accumulator holds the transposed 32x32 block: lane l has tile row (l & 31), register r
+    // has output column 8*(r >> 2) + 4*(l >> 5) + (r & 3) -- four adjacent columns per lane and
+    // register group, stored with one vector store.  The first K step of a tile starts from zero
+    // instead of from the accumulators (no separate clearing).
     typedef f32x16 Acc[NB][TM][TN];
-    auto mfmas = [&](Acc& acc, const Frags& f, auto nv) {
+    auto mfmas = [&](Acc& acc, const Frags& f, auto nv, auto first) {
+        const f32x16 zero = {};
 #pragma unroll
         for (int m = 0; m < NB; ++m)
 #pragma unroll
             for (int i = 0; i < decltype(nv)::value; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[m][j],
-                                                                          acc[m][i][j], 0, 0, 0);
+                    acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        f.b[m][j], f.a[i], decltype(first)::value ? zero : acc[m][i][j], 0, 0, 0);
             }
     };
+    const std::integral_constant<bool, true> first_step{};
+    const std::integral_constant<bool, false> later_step{};
     constexpr int NLD = A_INS + B_INS;           // direct-to-LDS loads per stage
-    constexpr int NLD0 = (NLD + 1) / 2;          // ... issued during step 0, the rest during step 1
+    // the first part of a stage's loads goes out during step 3 of the stage before, the rest
+    // during step 0; the first part holds A rows only, so that a tile's last two stages can
+    // switch the A offsets to the next tile before the B offsets
+    constexpr int NLD0 = (NLD + 1) / 2 < A_INS ? (NLD + 1) / 2 : A_INS;
     // Interleave one MFMA with the step's other instructions so that a single wave per SIMD keeps
     // the matrix core busy: MFMA, fragment read, MFMA, load, ...
     auto interleave = [&](int n_ds, int n_ld, auto nv) {
@@ -252,20 +347,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
             if (i < n_ld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
         }
     };
-    // A variant with NV sub-tiles per wave reads rows [0, NV * WGM * 32) of the A tile only, so
-    // its direct loads skip the rest (those LDS rows are never read).
-    auto issue_part = [&](bf16* st, int k0, int beg, int end, auto nv) {
+    // Loads of stage kidx of the current tile; kidx >= KT means stage kidx - KT of the next tile
+    // (the offsets and weight bases have been switched to it by then; without a chain these are
+    // in-bounds loads of the current tile into the idle slot, never used).  A variant with NV
+    // sub-tiles per wave reads rows [0, NV * WGM * 32) of its own A tile only, so its loads skip
+    // the rest; the next tile's loads take every row.
+    int kbase_c = cur.kpart * KT * FB_BK, kbase_n = kbase_c;
+    auto issue_part = [&](bf16* st, int kidx, int beg, int end, auto nv) {
         constexpr int A_NEED = decltype(nv)::value * WGM * 32 / (8 * NW);
+        const bool nxs = kidx >= KT;
+        const int k0 = nxs ? kbase_n + (chain ? (kidx - KT) * FB_BK : 0) : kbase_c + kidx * FB_BK;
+        const int a_need = nxs ? A_INS : A_NEED;
 #pragma unroll
         for (int q = 0; q < NLD; ++q) {
             if (q < beg || q >= end) continue;
-            if (q < A_INS && q >= A_NEED) continue;
             if (q < A_INS) {
+                if (q >= a_need) continue;
                 buffer_load_lds16(baseA, (lds_void_t*)(st + (8 * (wave + NW * q)) * 64), offA[q], 2 * k0);
             } else {
                 const int i = q - A_INS;
                 const int br0 = 8 * NW * i;
-                const char* bb = (NB == 2 && br0 >= BNH) ? baseB1 : baseB0;
+                const char* bb = uniform_ptr((NB == 2 && br0 >= BNH) ? baseB1 : baseB0);
                 buffer_load_lds16(bb, (lds_void_t*)(st + (BM + 8 * (wave + NW * i)) * 64), offB[i], 2 * k0);
             }
         }
@@ -274,94 +376,200 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     // first half of the next stage's loads is in flight.  The second half goes out during step 0;
     // the barrier sits before step 3, so the next stage's first fragments are read while step 3's
     // MFMAs run, and step 3 already sends the first half of the stage after next into the slot
-    // this stage has just released.  Loads past the last stage re-read K offset 0 into the idle
-    // slot (in bounds, never used), which keeps the schedule free of branches.
-    auto stage = [&](Acc& acc, bf16* cur, bf16* nxt, int k_next, int k_after, Frags& f0, Frags& f1, auto nv) {
+    // this stage has just released.
+    auto stage = [&](Acc& acc, bf16* cur_st, bf16* nxt_st, int k_next, int k_after, Frags& f0, Frags& f1, auto nv,
+                     auto first) {
         constexpr int NDS = decltype(nv)::value + NB * TN;   // fragment reads per K=16 step
-        load_frags(cur, 1, f1, nv);
-        issue_part(nxt, k_next, NLD0, NLD, nv);
-        mfmas(acc, f0, nv);
+        load_frags(cur_st, 1, f1, nv);
+        issue_part(nxt_st, k_next, NLD0, NLD, nv);
+        mfmas(acc, f0, nv, first);
         interleave(NDS, NLD - NLD0, nv);
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(cur, 2, f0, nv);
-        mfmas(acc, f1, nv);
+        load_frags(cur_st, 2, f0, nv);
+        mfmas(acc, f1, nv, later_step);
         interleave(NDS, 0, nv);
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(cur, 3, f1, nv);
-        mfmas(acc, f0, nv);
+        load_frags(cur_st, 3, f1, nv);
+        mfmas(acc, f0, nv, later_step);
         interleave(NDS, 0, nv);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0x0070);    // vmcnt(0) lgkmcnt(0): own loads and reads done
         __syncthreads();                       // next stage visible; this stage no longer read
-        load_frags(nxt, 0, f0, nv);
-        issue_part(cur, k_after, 0, NLD0, nv);
-        mfmas(acc, f1, nv);
+        load_frags(nxt_st, 0, f0, nv);
+        issue_part(cur_st, k_after, 0, NLD0, nv);
+        mfmas(acc, f1, nv, later_step);
         interleave(NDS, NLD0, nv);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    const int KT = a.K / FB_BK / a.ksplit;                 // stages of this K part
-    const int kbase = kpart * KT * FB_BK;
-    auto kofs = [&](int t) { return kbase + (t < KT ? t : 0) * FB_BK; };
-    // Epilogue.  32x32 C layout: lane holds column (lane & 31); register r holds row
-    // 8*(r >> 2) + 4*(lane >> 5) + (r & 3).
+    // The next tile's A sources (in-projection: x rows through perm) and row scales
+    // (out-projection: gate weights through perm) are loaded at the start of a tile and put in
+    // place after its first stage, so no load latency is waited for at a tile boundary.
+    TileInfo nx = cur;
+    int praw = 0;
+    float sc_next = 1.0f;
+    auto prefetch_next = [&]() {
+        const int r = nx.row_beg + nx.mt * BM + tid;
+        if (MODE == MODE_OUT) {
+            praw = (tid < BM && r < nx.row_end && a.row_scale && nx.seg < a.N) ? a.perm[r] : -1;
+        } else if (tid < BM) {
+            const int rc = r < nx.row_end ? r : nx.row_beg + nx.mt * BM;
+            praw = (nx.seg < a.N) ? a.perm[rc] : rc;
+        }
+    };
+    auto after_first_stage = [&]() {
+        if (MODE == MODE_OUT) sc_next = praw >= 0 ? a.row_scale[praw] : 1.0f;
+        else if (tid < BM) s_src[tid] = (nx.seg < a.N) ? praw / a.k : praw - a.T * a.k;
+    };
+    auto switch_a = [&]() {                              // A offsets of the next tile
+        const int l = fresh_lane();
+        const uint32_t lc = (uint32_t)(((l & 7) ^ ((4 * wave + (l >> 4)) & 7)) * 8);
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i) {
+            const int src = (MODE == MODE_OUT) ? a_row(nx, i, l) : s_src[8 * (wave + NW * i) + (l >> 3)];
+            offA[i] = ((uint32_t)src * (uint32_t)a.K + lc) * 2u;
+        }
+    };
+
+    // Epilogue (transposed accumulator layout, see mfmas): per sub-tile one row per lane and
+    // four groups of four adjacent columns, each written with one 8-byte (bf16) or 16-byte
+    // (fp32) store.  Ncols is a multiple of 64, so a group is either inside or past the end.
     auto store = [&](const Acc& acc, auto nv) {
+        const int m0 = cur.row_beg + cur.mt * BM, n0 = cur.nt * BNH;
+        const float* scl = s_scale + (MODE == MODE_OUT ? (it & 1) * BM : 0);
+        // computed here, not hoisted above the K loop where they would hold registers
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int c0 = n0 + wn * Cfg::WTN;             // this wave's first column
 #pragma unroll
         for (int i = 0; i < decltype(nv)::value; ++i) {
+            const int rl = (i * WGM + wm) * 32 + (ln & 31);
+            const int row = m0 + rl;
+            if (row >= cur.row_end) continue;
+            const float scale = (MODE == MODE_OUT) ? scl[rl] : 1.0f;
+            // this lane's row at its first group of four columns; the groups follow at constant
+            // offsets (immediate offsets of the stores)
+            const size_t base = (size_t)row * a.Ncols + c0 + 4 * (ln >> 5);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + (i * WGM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row >= row_end) continue;
-                const float scale = (MODE == MODE_OUT) ? s_scale[row - m0] : 1.0f;
+            for (int j = 0; j < TN; ++j) {
+                if (c0 + j * 32 >= a.Ncols) continue;   // whole 32-column blocks (Ncols % 64 == 0)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
-                    if (col >= a.Ncols) continue;
-                    float v;
-                    if (MODE == MODE_IN_SWIGLU) v = silu_f32(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
-                    else if (MODE == MODE_IN_RELU) v = fmaxf(acc[0][i][j][r], 0.f);
-                    else v = acc[0][i][j][r] * scale;
-                    if (MODE == MODE_OUT) ((float*)a.C)[kpart * a.part_stride + (size_t)row * a.Ncols + col] = v;
-                    else ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)v;
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = acc[0][i][j][4 * g + e];
+                        if (MODE == MODE_IN_SWIGLU) v[e] = silu_f32(x) * acc[NB - 1][i][j][4 * g + e];
+                        else if (MODE == MODE_IN_RELU) v[e] = fmaxf(x, 0.f);
+                        else v[e] = x * scale;
+                    }
+                    if (MODE == MODE_OUT) {
+                        float4 o = {v[0], v[1], v[2], v[3]};
+                        *(float4*)((float*)a.C + cur.kpart * a.part_stride + base + j * 32 + 8 * g) = o;
+                    } else {
+                        uint2 o;
+                        o.x = pack_bf16x2(v[0], v[1]);
+                        o.y = pack_bf16x2(v[2], v[3]);
+                        *(uint2*)((bf16*)a.C + base + j * 32 + 8 * g) = o;
+                    }
                 }
+                // one 32x32 block at a time keeps the epilogue's registers few
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
-    // Each variant owns its accumulators and epilogue, so no accumulator is live across the
-    // choice of variant.
+    // One tile.  The tile's 32-row sub-tiles are dealt to the wave rows in turn (sub-tile s to
+    // wave row s % WGM), so the rows of a short tile (an expert's last one) spread over all
+    // waves; a tile whose valid sub-tiles fit in NV per wave runs the variant with NV sub-tiles
+    // per wave and skips the MFMAs and fragment reads of the rest (rows past the end were loaded
+    // as copies of the first row and are never stored).  Each variant owns its accumulators and
+    // epilogue, so no accumulator is live across the choice of variant.  On entry the tile's
+    // first stage and half of its second are loaded or in flight.
     auto run = [&](auto nv) {
         Acc acc;
-#pragma unroll
-        for (int m = 0; m < NB; ++m)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
         Frags fa, fb;
-        // the out-projection's row scales are fetched once per tile, while the first stage loads
-        float sc = 1.0f;
-        if (MODE == MODE_OUT && tid < BM && m0 + tid < row_end && a.row_scale && seg < a.N)
-            sc = a.row_scale[a.perm[m0 + tid]];
-        issue_part(st0, kbase, 0, NLD, nv);
         __builtin_amdgcn_s_waitcnt(0x0070);
-        if (MODE == MODE_OUT && tid < BM) s_scale[tid] = sc;
         __syncthreads();
+        if (chain) prefetch_next();
         load_frags(st0, 0, fa, nv);
-        issue_part(st1, kofs(1), 0, NLD0, nv);
-        int kt = 0;
-        for (; kt + 2 <= KT; kt += 2) {
-            stage(acc, st0, st1, kofs(kt + 1), kofs(kt + 2), fa, fb, nv);
-            stage(acc, st1, st0, kofs(kt + 2), kofs(kt + 3), fa, fb, nv);
+        if (chain) {
+            stage(acc, st0, st1, 1, 2, fa, fb, nv, first_step);
+            after_first_stage();
+            stage(acc, st1, st0, 2, 3, fa, fb, nv, later_step);
+            for (int kt = 2; kt + 4 <= KT; kt += 2) {
+                stage(acc, st0, st1, kt + 1, kt + 2, fa, fb, nv, later_step);
+                stage(acc, st1, st0, kt + 2, kt + 3, fa, fb, nv, later_step);
+            }
+            // the last two stages send out the next tile's first stage and half of its second
+            switch_a();
+            stage(acc, st0, st1, KT - 1, KT, fa, fb, nv, later_step);
+            set_b(nx);
+            stage(acc, st1, st0, KT, KT + 1, fa, fb, nv, later_step);
+        } else {
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
+            int kt = 0;
+            for (; kt + 2 <= KT; kt += 2) {
+                stage(acc, st0, st1, kt + 1, kt + 2, fa, fb, nv, later_step);
+                stage(acc, st1, st0, kt + 2, kt + 3, fa, fb, nv, later_step);
+            }
+            if (kt < KT) stage(acc, st0, st1, KT, KT + 1, fa, fb, nv, later_step);
         }
-        if (kt < KT) stage(acc, st0, st1, kbase, kbase, fa, fb, nv);
-        __builtin_amdgcn_s_waitcnt(0x0070);    // no load may still be writing LDS at exit
         store(acc, nv);
+        // the next tile's offsets again (cheap), so that none is held through the epilogue
+        if (chain) {
+            switch_a();
+            set_b(nx);
+        }
     };
-    if (TM >= 2 && nsub <= WGM) run(std::integral_constant<int, 1>{});
-    else if (TM >= 4 && nsub <= 2 * WGM) run(std::integral_constant<int, 2>{});
-    else run(std::integral_constant<int, TM>{});
+    auto run_tile = [&]() {
+        const int nsub = (cur.row_end - (cur.row_beg + cur.mt * BM) + 31) / 32;
+        if (TM >= 2 && nsub <= WGM) run(std::integral_constant<int, 1>{});
+        else if (TM >= 4 && nsub <= 2 * WGM) run(std::integral_constant<int, 2>{});
+        else run(std::integral_constant<int, TM>{});
+    };
+
+    // first tile: everything loaded here
+    set_a_direct(cur);
+    set_b(cur);
+    if (MODE == MODE_OUT && tid < BM) s_scale[tid] = scale_of(cur);
+    issue_part(st0, 0, 0, NLD, std::integral_constant<int, TM>{});
+    issue_part(st1, 1, 0, NLD0, std::integral_constant<int, TM>{});
+    for (;;) {
+        const bool has_next = tile_id(it + 1) < hi;
+        if (has_next && ((it + 1) & 63) == 0) {
+            // every wave has taken its tiles of the previous 64 from s_tiles (one tile back)
+            if (wave == 0) decode_chunk((it + 1) >> 6);
+            __syncthreads();
+        }
+        nx = has_next ? read_tile(it + 1) : cur;
+        kbase_n = nx.kpart * KT * FB_BK;
+        run_tile();
+        if (!has_next) break;
+        if (!chain) {
+            // no chain: the next tile's first loads go out after every wave is done with this one
+            __builtin_amdgcn_s_waitcnt(0x0070);
+            __syncthreads();
+            set_a_direct(nx);
+            set_b(nx);
+            sc_next = (MODE == MODE_OUT) ? scale_of(nx) : 1.0f;
+            kbase_c = kbase_n;
+            issue_part(st0, 0, 0, NLD, std::integral_constant<int, TM>{});
+            issue_part(st1, 1, 0, NLD0, std::integral_constant<int, TM>{});
+        }
+        // the next tile's epilogue comes after at least one more barrier
+        if (MODE == MODE_OUT && tid < BM) s_scale[((it + 1) & 1) * BM + tid] = sc_next;
+        cur = nx;
+        kbase_c = kbase_n;
+        ++it;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);    // no load may still be writing LDS at exit
 }
 
 // ------------------------------------------------------------------ skinny path (decode)
@@ -526,6 +734,23 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------------ launchers
+// Blocks of one kernel that the device keeps resident at once (a multiple of 8, one share per
+// XCD), found once per device.
+template <typename K>
+static int resident_blocks(K kern, int threads) {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess) return 0;
+    int v = (cus * (per_cu > 0 ? per_cu : 1)) / 8 * 8;
+    if (v < 8) v = 8;
+    if (dev >= 0 && dev < 64) cache[dev] = v;
+    return v;
+}
+
 template <int MODE, int BM, int BNH, int WGM, int WGN>
 static hipError_t launch_bf16(const FfnKArgs& ka, hipStream_t s) {
     using Cfg = FfnTile<MODE, BM, BNH, WGM, WGN>;
@@ -534,7 +759,10 @@ static hipError_t launch_bf16(const FfnKArgs& ka, hipStream_t s) {
     if (a.ksplit < 1) a.ksplit = 1;
     a.mt_max = (a.T * a.k + BM - 1) / BM + a.N + (a.has_shared ? (a.T + BM - 1) / BM : 0);
     a.n_tiles = (a.Ncols + BNH - 1) / BNH;
-    const long long G = 8 * (((long long)a.mt_max * a.n_tiles * a.ksplit + 7) / 8);
+    const int resident = resident_blocks(kern, Cfg::NT);
+    if (resident <= 0) return hipErrorInvalidDevice;
+    long long G = 8 * (((long long)a.mt_max * a.n_tiles * a.ksplit + 7) / 8);   // one tile per block at most
+    if (G > resident) G = resident;
     hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), 0, s, a);
     return hipGetLastError();
 }
