@@ -89,9 +89,19 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, lds_void_t* 
 // next to an expert's short last one) does not fall on the same blocks every round.
 #define FFN_MAX_SEG 320   // 5 segments per lane of one wave: routed experts and the shared one
 
-template <int BM>
-__device__ __forceinline__ void build_segments(const FfnKArgs& a, int lane, int* s_tab, int* s_R1) {
-    int tl[5], beg[5], rows[5], loc = 0;
+// Estimated cost of a tile in 1/256 of a full tile: a short tile (an expert's last m-tile) runs
+// the variant with fewer sub-tiles per wave and costs about half a full tile plus its share of
+// the MFMAs (measured: a 64-row tile of 256 takes 0.65 of a full one).
+template <int TM, int WGM>
+__device__ __forceinline__ int tile_cost(int rows_in_tile) {
+    const int nsub = (rows_in_tile + 31) / 32;
+    const int nv = (TM >= 2 && nsub <= WGM) ? 1 : (TM >= 4 && nsub <= 2 * WGM) ? 2 : TM;
+    return 128 + 128 * nv / TM;
+}
+
+template <int BM, int TM, int WGM>
+__device__ __forceinline__ void build_segments(const FfnKArgs& a, int lane, int* s_tab, int* s_R1, int* s_C1) {
+    int tl[5], beg[5], rows[5], cost[5], loc = 0, cloc = 0;
 #pragma unroll
     for (int q = 0; q < 5; ++q) {
         const int s = lane * 5 + q;
@@ -105,15 +115,22 @@ __device__ __forceinline__ void build_segments(const FfnKArgs& a, int lane, int*
             rows[q] = a.T;
         }
         tl[q] = (rows[q] + BM - 1) / BM;
+        const int part = rows[q] % BM;
+        cost[q] = a.n_tiles * ((rows[q] / BM) * 256 + (part ? tile_cost<TM, WGM>(part) : 0));
         loc += tl[q];
+        cloc += cost[q];
     }
-    int incl = loc;
+    int incl = loc, cincl = cloc;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
+        const int w = __shfl_up(cincl, o, 64);
+        if (lane >= o) {
+            incl += v;
+            cincl += w;
+        }
     }
-    int run = incl - loc;
+    int run = incl - loc, crun = cincl - cloc;
 #pragma unroll
     for (int q = 0; q < 5; ++q) {
         const int s = lane * 5 + q;
@@ -121,9 +138,43 @@ __device__ __forceinline__ void build_segments(const FfnKArgs& a, int lane, int*
         s_tab[FFN_MAX_SEG + s] = tl[q];
         s_tab[2 * FFN_MAX_SEG + s] = beg[q];
         s_tab[3 * FFN_MAX_SEG + s] = beg[q] + rows[q];
+        s_tab[4 * FFN_MAX_SEG + s] = crun;
         run += tl[q];
+        crun += cost[q];
     }
-    if (lane == 63) *s_R1 = incl * a.n_tiles;
+    if (lane == 63) {
+        *s_R1 = incl * a.n_tiles;
+        *s_C1 = cincl;
+    }
+}
+
+// The XCDs' shares of the tile numbering, split by estimated cost rather than by count (an
+// XCD whose share holds no short tiles would otherwise finish last): lane x of wave 0 finds
+// where cost x/8 of the whole starts, as the segment holding it and the tile at that fraction
+// of the segment's cost.
+__device__ __forceinline__ void xcd_bounds(const FfnKArgs& a, const int* s_tab, int R1, int C1, int lane, int* s_bound) {
+    if (lane > 8) return;
+    const int R = R1 * a.ksplit;
+    if (lane == 8 || C1 == 0) {
+        s_bound[lane] = lane == 8 ? R : 0;
+        return;
+    }
+    const long long b = (long long)C1 * a.ksplit * lane / 8;
+    const int kp = (int)(b / C1);
+    const int rem = (int)(b - (long long)kp * C1);
+    int lo = 0, hi = a.N + (a.has_shared ? 1 : 0) - 1;
+    while (lo < hi) {                                  // last segment whose cost starts <= rem
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tab[4 * FFN_MAX_SEG + mid] <= rem) lo = mid;
+        else hi = mid - 1;
+    }
+    const int tiles = s_tab[FFN_MAX_SEG + lo] * a.n_tiles;
+    // (segments past the last one have zero cost, so lo + 1 always has a cost start)
+    const int seg_c = s_tab[4 * FFN_MAX_SEG + lo + 1] - s_tab[4 * FFN_MAX_SEG + lo];
+    int off = seg_c > 0 ? (int)((long long)(rem - s_tab[4 * FFN_MAX_SEG + lo]) * tiles / seg_c) : 0;
+    off = off < tiles ? off : tiles;
+    const int t = kp * R1 + s_tab[lo] + off;
+    s_bound[lane] = t < R ? t : R;
 }
 
 // Two floats rounded to bf16 (nearest even, as a bf16 conversion) in one 32-bit word, the
@@ -192,20 +243,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     // stage from the asynchronous loads into the other
     __shared__ __attribute__((aligned(1024))) bf16 st0[ROWS * 64];
     __shared__ __attribute__((aligned(1024))) bf16 st1[ROWS * 64];
-    __shared__ int s_tab[4 * FFN_MAX_SEG];
-    __shared__ int s_R1;
+    __shared__ int s_tab[5 * FFN_MAX_SEG];
+    __shared__ int s_R1, s_C1;
+    __shared__ int s_bound[9];                                 // the XCDs' shares of the tiles
     __shared__ int s_tiles[64 * 6];                            // this block's next 64 tiles
     __shared__ int s_src[MODE == MODE_OUT ? 1 : BM];          // next tile's x row of each A row
     __shared__ float s_scale[MODE == MODE_OUT ? 2 * BM : 1];  // gate weight of each row, 2 tiles
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go to M0
-    if (wave == 0) build_segments<BM>(a, lane, s_tab, &s_R1);
+    static_assert(FFN_MAX_SEG > MOE_MAX_EXPERTS + 1, "a zero-cost entry follows the last segment");
+    if (wave == 0) build_segments<BM, TM, WGM>(a, lane, s_tab, &s_R1, &s_C1);
+    __syncthreads();
+    if (wave == 0) xcd_bounds(a, s_tab, s_R1, s_C1, lane, s_bound);
     __syncthreads();
     const int R1 = __builtin_amdgcn_readfirstlane(s_R1);
-    const int R = R1 * a.ksplit;
     const int nbx = gridDim.x >> 3, xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
-    const int per = (R + 7) >> 3, lo = xcd * per, hi = min(R, lo + per);
+    const int lo = __builtin_amdgcn_readfirstlane(s_bound[xcd]), hi = __builtin_amdgcn_readfirstlane(s_bound[xcd + 1]);
     auto tile_id = [&](int i) { return lo + i * nbx + ((i & 1) ? nbx - 1 - jb : jb); };
     int it = 0;                                          // tiles done by this block
     if (tile_id(0) >= hi) return;
