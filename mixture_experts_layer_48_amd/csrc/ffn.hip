@@ -296,7 +296,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
 
     // per-lane 32-bit byte offsets of this wave's load instructions from a uniform base
     // (x / H stay below 4 GiB, one expert's weight matrix too)
-    const int lrow = lane >> 3;                          // row within the 8-row group
     // Lane-derived values are recomputed where a tile's offsets are set (an empty asm hides the
     // lane id from the optimiser there), instead of being precomputed once per row group and
     // held in registers for the whole kernel.
@@ -628,21 +627,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
 
 // ------------------------------------------------------------------ skinny path (decode)
 // For a few rows per expert the GEMMs are weight streams: every weight byte of a touched expert
-// is read once and used for at most 16 rows.  One wave owns one 16-column group of one segment
+// is read once and used for at most 16 rows.  One wave owns CG 16-column groups of one segment
 // and the whole K range; its B fragments (16 weight rows x 32 K for v_mfma_f32_16x16x32_bf16)
 // come straight from memory into registers, U steps at a time, and its A fragments (the <= 16
-// rows, gathered through perm for the in-projection) are shared by all waves through L2.  Waves
-// are numbered segment, then column group, so the waves of a block stream neighbouring weight
-// rows.  Empty experts are skipped, so only touched
+// rows, gathered through perm for the in-projection) serve all CG groups and are shared by all
+// waves through L2.  Waves are numbered segment, then column group, so the waves of a block
+// stream neighbouring weight rows.  Empty experts are skipped, so only touched
 // experts' weights are read.  Segments with more than 16 rows loop over 16-row tiles.  (Weight
 // loads stay cached: a load instruction covers half of each 128-byte line it touches and the
 // next K step reads the other half; non-temporal loads measured slower.)
-template <int MODE, int U>
+template <int MODE, int U, int CG>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
     constexpr int NB = (MODE == MODE_IN_SWIGLU) ? 2 : 1;
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);        // global wave id
-    const int ngroups = (a.Ncols + 15) / 16;
+    const int ngroups = (a.Ncols + 16 * CG - 1) / (16 * CG);
     const int nseg = a.N + (a.has_shared ? 1 : 0);
     const int seg = gw / ngroups, cg = gw % ngroups;
     if (seg >= nseg) return;
@@ -662,11 +661,17 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
     }
     if (row_end <= row_beg) return;                             // expert not touched
     const int KS = a.K / 32;
-    const int col = cg * 16 + (lane & 15);                      // this lane's B column
-    const int colc = col < a.Ncols ? col : a.Ncols - 1;
     const int kq = (lane >> 4) * 8;                             // this lane's K offset in a step
-    const bf16* pb0 = B0 + (size_t)colc * a.K + kq;
-    const bf16* pb1 = (NB == 2) ? B1 + (size_t)colc * a.K + kq : nullptr;
+    // this lane's B columns: one per 16-column group of the wave
+    const bf16* pb0[CG];
+    const bf16* pb1[CG];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+        const int col = (cg * CG + c) * 16 + (lane & 15);
+        const int colc = col < a.Ncols ? col : a.Ncols - 1;
+        pb0[c] = B0 + (size_t)colc * a.K + kq;
+        pb1[c] = (NB == 2) ? B1 + (size_t)colc * a.K + kq : nullptr;
+    }
     for (int m0 = row_beg; m0 < row_end; m0 += 16) {
         const int r = m0 + (lane & 15);                         // this lane's A row
         const bool rok = r < row_end;
@@ -674,64 +679,85 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
         if (MODE == MODE_OUT) src = rok ? r : m0;
         else src = (seg < a.N) ? a.perm[rok ? r : m0] / a.k : (rok ? r : m0) - a.T * a.k;
         const bf16* pa = a.A + (size_t)src * a.K + kq;
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc0[CG], acc1[CG];
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+            acc0[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            acc1[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
         const bf16x8 zero8 = {};
         int ks = 0;
         for (; ks + U <= KS; ks += U) {
-            bf16x8 b0[U], b1[U], av[U];
+            bf16x8 b0[U][CG], b1[U][CG], av[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                b0[u] = *(const bf16x8*)(pb0 + (ks + u) * 32);
-                if (NB == 2) b1[u] = *(const bf16x8*)(pb1 + (ks + u) * 32);
+#pragma unroll
+                for (int c = 0; c < CG; ++c) {
+                    b0[u][c] = *(const bf16x8*)(pb0[c] + (ks + u) * 32);
+                    if (NB == 2) b1[u][c] = *(const bf16x8*)(pb1[c] + (ks + u) * 32);
+                }
                 av[u] = rok ? *(const bf16x8*)(pa + (ks + u) * 32) : zero8;
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b0[u], acc0, 0, 0, 0);
-                if (NB == 2) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b1[u], acc1, 0, 0, 0);
-            }
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int c = 0; c < CG; ++c) {
+                    acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b0[u][c], acc0[c], 0, 0, 0);
+                    if (NB == 2) acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b1[u][c], acc1[c], 0, 0, 0);
+                }
         }
         for (; ks < KS; ++ks) {
-            const bf16x8 b0 = *(const bf16x8*)(pb0 + ks * 32);
             const bf16x8 av = rok ? *(const bf16x8*)(pa + ks * 32) : zero8;
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0, acc0, 0, 0, 0);
-            if (NB == 2) {
-                const bf16x8 b1 = *(const bf16x8*)(pb1 + ks * 32);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1, acc1, 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+                const bf16x8 b0 = *(const bf16x8*)(pb0[c] + ks * 32);
+                acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0, acc0[c], 0, 0, 0);
+                if (NB == 2) {
+                    const bf16x8 b1 = *(const bf16x8*)(pb1[c] + ks * 32);
+                    acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1, acc1[c], 0, 0, 0);
+                }
             }
         }
         // 16x16 C layout: lane holds column (lane & 15), rows 4 * (lane >> 4) + i
-        if (col < a.Ncols) {
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+            const int col = (cg * CG + c) * 16 + (lane & 15);
+            if (col >= a.Ncols) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = m0 + 4 * (lane >> 4) + i;
                 if (row >= row_end) continue;
                 if (MODE == MODE_OUT) {
                     const float scale = (a.row_scale && seg < a.N) ? a.row_scale[a.perm[row]] : 1.0f;
-                    ((float*)a.C)[(size_t)row * a.Ncols + col] = acc0[i] * scale;
+                    ((float*)a.C)[(size_t)row * a.Ncols + col] = acc0[c][i] * scale;
                 } else if (MODE == MODE_IN_SWIGLU) {
-                    ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)(silu_f32(acc0[i]) * acc1[i]);
+                    ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)(silu_f32(acc0[c][i]) * acc1[c][i]);
                 } else {
-                    ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)fmaxf(acc0[i], 0.f);
+                    ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)fmaxf(acc0[c][i], 0.f);
                 }
             }
         }
     }
 }
 
-template <int MODE, int U>
+template <int MODE, int U, int CG>
 static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
-    const long long waves = (long long)(a.N + (a.has_shared ? 1 : 0)) * ((a.Ncols + 15) / 16);
-    auto kern = ffn_skinny_kernel<MODE, U>;
+    const long long waves = (long long)(a.N + (a.has_shared ? 1 : 0)) * ((a.Ncols + 16 * CG - 1) / (16 * CG));
+    auto kern = ffn_skinny_kernel<MODE, U, CG>;
     hipLaunchKernelGGL(kern, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 // Decode-sized batches (at most 16 rows per expert on average) take the weight-streaming path.
-// Unroll depths: the in-projection's shallower unroll keeps its registers low enough that all of
-// its waves are resident at once.
+// Unroll depths and 16-column groups per wave (measured on the Mixtral decode layer): the
+// in-projection keeps one group and a shallow unroll, so that its registers stay low enough for
+// all of its waves to be resident at once (two groups: 0.38 vs 0.35 ms); the out-projection
+// takes two groups per wave, which halves its activation loads (0.17 vs 0.18 ms; four groups
+// leave too few waves for d = 4096).
 #define SK_U_IN 4
-#define SK_U_OUT 8
+#define SK_CG_IN 1
+#define SK_U_OUT 4
+#define SK_CG_OUT 2
 static bool skinny(const FfnLaunch& f) { return (long long)f.T * f.k <= 16LL * f.N; }
 
 // ------------------------------------------------------------------ fp32 path
@@ -853,13 +879,13 @@ hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
         if (f.ffn == 1) {
             a.B0 = (const bf16*)f.w_gate; a.B1 = (const bf16*)f.w_up;
             a.S0 = (const bf16*)f.sh_gate; a.S1 = (const bf16*)f.sh_up;
-            if (skinny(f)) return launch_skinny<MODE_IN_SWIGLU, SK_U_IN>(a, s);
+            if (skinny(f)) return launch_skinny<MODE_IN_SWIGLU, SK_U_IN, SK_CG_IN>(a, s);
             if (big_tiles(f)) return launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, s);
             return launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, s);
         }
         a.B0 = (const bf16*)f.w_up;
         a.S0 = (const bf16*)f.sh_up;
-        if (skinny(f)) return launch_skinny<MODE_IN_RELU, SK_U_IN>(a, s);
+        if (skinny(f)) return launch_skinny<MODE_IN_RELU, SK_U_IN, SK_CG_IN>(a, s);
         if (big_tiles(f)) return launch_bf16<MODE_IN_RELU, 256, 256, 2, 2>(a, s);
         return launch_bf16<MODE_IN_RELU, 128, 128, 2, 2>(a, s);
     }
@@ -891,7 +917,7 @@ hipError_t launch_ffn_out(const FfnLaunch& f, hipStream_t s) {
         a.K = f.d_ff; a.Ncols = f.d;
         a.ksplit = f.ksplit;
         a.part_stride = (long long)((long long)f.T * f.k + (f.has_shared ? f.T : 0)) * f.d;
-        if (skinny(f)) return launch_skinny<MODE_OUT, SK_U_OUT>(a, s);
+        if (skinny(f)) return launch_skinny<MODE_OUT, SK_U_OUT, SK_CG_OUT>(a, s);
         if (big_tiles(f)) return launch_bf16<MODE_OUT, 256, 256, 2, 2>(a, s);
         return launch_bf16<MODE_OUT, 128, 128, 2, 2>(a, s);
     }
