@@ -83,6 +83,11 @@ SMALL = {
     "skinny_capacity": W.LayerConfig("skinny_capacity", T=64, d=128, N=16, k=2, d_ff=256, dtype="bf16",
                                      ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, capacity_factor=1.0,
                                      zipf_bias=True, seed=20),
+    # the named routing variants at small widths: top-1 over 128 ReLU experts (about 23 rows
+    # each, the 128-row tiles), top-1 over 16 SwiGLU experts, shared expert + top-7 of 256
+    "switch_small": C["switch_top1"].replace(name="switch_small", T=3000, d=128, d_ff=256),
+    "scout_small": C["scout_top1"].replace(name="scout_small", T=600, d=256, d_ff=384),
+    "v4_small": C["v4_shared_top7"].replace(name="v4_small", T=260, d=128, d_ff=192),
 }
 
 
@@ -174,8 +179,10 @@ def test_stage_entry_points_compose_to_forward():
     _free()
 
 
-FULL = ["mixtral_prefill", "mixtral_decode", "deepseek_v3", "skewed_capacity"]
-SAMPLE_TOKENS = {"mixtral_prefill": 8, "mixtral_decode": 16, "deepseek_v3": 4, "skewed_capacity": 8}
+FULL = ["mixtral_prefill", "mixtral_decode", "deepseek_v3", "skewed_capacity", "switch_top1", "scout_top1",
+        "v4_shared_top7"]
+SAMPLE_TOKENS = {"mixtral_prefill": 8, "mixtral_decode": 16, "deepseek_v3": 4, "skewed_capacity": 8,
+                 "switch_top1": 8, "scout_top1": 8, "v4_shared_top7": 4}
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -105,6 +105,17 @@ CONFIGS: Dict[str, LayerConfig] = {
     "skewed_capacity": LayerConfig("skewed_capacity", T=16384, d=3584, N=128, k=2, d_ff=2560,
                                    dtype="bf16", ffn=FFN_SWIGLU, gating=GATE_TOPK_SOFTMAX,
                                    capacity_factor=2.0, zipf_bias=True, seed=1005),
+    # Routing variants the pages name without layer widths (those are taken from the layers
+    # above): top-1 over 128 experts with two-layer ReLU experts (Switch-style), top-1 over 16
+    # SwiGLU experts (Llama 4 Scout-style), and one shared expert plus top-7 of 256 routed ones
+    # (the DeepSeek-V4 description: 8 active experts, the shared one included).
+    "switch_top1": LayerConfig("switch_top1", T=4096, d=4096, N=128, k=1, d_ff=14336,
+                               dtype="bf16", ffn=FFN_RELU2, gating=GATE_TOPK_SOFTMAX, seed=1006),
+    "scout_top1": LayerConfig("scout_top1", T=4096, d=4096, N=16, k=1, d_ff=14336,
+                              dtype="bf16", ffn=FFN_SWIGLU, gating=GATE_TOPK_SOFTMAX, seed=1007),
+    "v4_shared_top7": LayerConfig("v4_shared_top7", T=8192, d=7168, N=256, k=7, d_ff=2048,
+                                  dtype="bf16", ffn=FFN_SWIGLU, gating=GATE_SOFTMAX_TOPK,
+                                  has_shared=True, seed=1008),
 }
 
 
