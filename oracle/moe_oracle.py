@@ -55,7 +55,7 @@ __all__ = [
     "TOPK_SOFTMAX", "SOFTMAX_TOPK", "RELU2", "SWIGLU", "LINEAR",
     "router_logits", "rank_experts", "gate_weights", "topk_route", "expert_capacity",
     "capacity_route", "route_from_logits", "group_by_expert", "silu", "expert_ffn",
-    "combine", "forward", "param_counts", "near_tie_tokens",
+    "combine", "forward", "param_counts", "near_tie_tokens", "routing_stats",
 ]
 
 
@@ -312,3 +312,50 @@ def near_tie_tokens(z, depth: int, threshold: float = 1e-6) -> np.ndarray:
     depth = min(depth, z.shape[1] - 1)
     gaps = zs[:, :depth] - zs[:, 1:depth + 1]
     return np.nonzero((gaps < threshold).any(axis=1))[0]
+
+
+
+# ---------------------------------------------------------------- routing health
+def routing_stats(z, idx, counts, alpha: float = 0.01) -> Dict[str, object]:
+    """Health statistics of one layer call's routing.
+
+    From [P5] §4.2 (路由质量诊断): the entropy in bits of the experts' share of
+    the routed slots (log2 N when every expert gets the same share), the three
+    most used experts and their share of the slots, and the ratio of the
+    standard deviation of the per-expert counts to their mean (the term of its
+    online calibration).  From [P3] (核心机制, the load-balancing loss): the
+    value alpha * N * sum_i f_i * p_i, with f_i expert i's share of the routed
+    slots and p_i its routing probability averaged over the tokens (softmax over
+    all N logits).  From [P5] §2.2 (expert capacity) and §3.3 (its re-route rate): the share of slots
+    that did not get their own ranked choice (slot j of a token not holding the
+    token's j-th ranked expert, a dropped slot included).
+
+    Readings: shares are of the kept slots (the counts); empty experts add 0 to
+    the entropy; the standard deviation is the population one (over the N
+    experts); ties among the three most used experts go to the lower id; with
+    fewer than three experts the missing ids are -1.
+    """
+    z = _f64(z)
+    idx = np.asarray(idx, dtype=np.int64)
+    c = np.asarray(counts, dtype=np.float64)
+    T, N = z.shape
+    k = idx.shape[1]
+    S = c.sum()
+    share = c / S
+    nz = share > 0
+    entropy = float(-(share[nz] * np.log2(share[nz])).sum())
+    order = np.lexsort((np.arange(N), -c))              # count descending, then id ascending
+    top = [int(e) for e in order[:3]] + [-1] * max(0, 3 - N)
+    top3_share = float(c[order[:3]].sum() / S)
+    mean = S / N
+    cv = float(math.sqrt(((c - mean) ** 2).mean()) / mean)
+    zm = z.max(axis=1, keepdims=True)
+    p = np.exp(z - zm)
+    p /= p.sum(axis=1, keepdims=True)
+    p_mean = p.mean(axis=0)
+    balance = float(alpha * N * (share * p_mean).sum())
+    ranked = rank_experts(z)[:, :k]
+    rerouted = int((idx != ranked).sum())
+    return dict(entropy_bits=entropy, entropy_ideal_bits=math.log2(N), top3_share=top3_share,
+                max_share=float(share.max()), cv=cv, balance_loss=balance,
+                reroute_rate=rerouted / float(T * k), experts_touched=int((c > 0).sum()), top3=top)

@@ -376,3 +376,77 @@ def test_near_tie_detection():
     z = np.array([[1.0, 1.0 + 5e-7, 0.0], [3.0, 2.0, 1.0], [0.0, 0.5, 0.5 + 2e-6]])
     assert O.near_tie_tokens(z, depth=1).tolist() == [0]
     assert O.near_tie_tokens(z, depth=2, threshold=3e-6).tolist() == [0, 2]
+
+
+# ---------------------------------------------------------------- routing health statistics
+def _uniform_routing(T, N, k):
+    """Token t takes experts (t*k + j) mod N in slot j: every expert gets T*k/N slots when N
+    divides T*k; logits rank exactly those experts first."""
+    idx = np.array([[(t * k + j) % N for j in range(k)] for t in range(T)])
+    z = np.zeros((T, N))
+    for t in range(T):
+        for j in range(k):
+            z[t, idx[t, j]] = 10.0 - j
+    counts = np.bincount(idx.ravel(), minlength=N)
+    return z, idx, counts
+
+
+def test_routing_entropy_of_uniform_128_experts_is_the_printed_ideal():
+    for N, val, dec in ((int(r[0]), float(r[1]), int(r[2])) for r in _golden_rows("router_entropy.txt")):
+        z, idx, counts = _uniform_routing(T=N * 4, N=N, k=2)
+        st = O.routing_stats(z, idx, counts)
+        assert round(st["entropy_bits"], dec) == val
+        assert st["entropy_bits"] == pytest.approx(st["entropy_ideal_bits"], abs=1e-12)
+        assert st["top3_share"] == pytest.approx(3.0 / N) and st["cv"] == pytest.approx(0.0, abs=1e-15)
+        assert st["reroute_rate"] == 0.0 and st["experts_touched"] == N
+
+
+def test_routing_stats_all_slots_on_one_expert():
+    T, N = 12, 8
+    z = np.full((T, N), -1.0)
+    z[:, 5] = 3.0
+    idx = np.full((T, 1), 5)
+    counts = np.bincount(idx.ravel(), minlength=N)
+    st = O.routing_stats(z, idx, counts)
+    assert st["entropy_bits"] == 0.0 and st["top3_share"] == 1.0 and st["max_share"] == 1.0
+    assert st["top3"] == [5, 0, 1]                     # ties among the empty experts: lower id first
+    assert st["cv"] == pytest.approx(math.sqrt(N - 1))  # counts (0,..,T,..,0): std = T*sqrt(N-1)/N, mean = T/N
+
+
+def test_routing_stats_hand_worked_counts():
+    # two experts with counts 3 and 1: shares 3/4 and 1/4, entropy 2 - (3/4) log2 3, mean 2, std 1
+    z = np.array([[1.0, 0.0]] * 3 + [[0.0, 1.0]])
+    idx = np.array([[0], [0], [0], [1]])
+    st = O.routing_stats(z, idx, np.array([3, 1]))
+    assert st["entropy_bits"] == pytest.approx(2.0 - 0.75 * math.log2(3.0), abs=1e-15)
+    assert st["cv"] == pytest.approx(0.5) and st["top3"] == [0, 1, -1] and st["top3_share"] == 1.0
+    # p_0 averaged over tokens = (3 s + (1 - s)) / 4 with s = e/(1+e); loss = a*N*(3/4 p_0 + 1/4 p_1)
+    s = math.e / (1.0 + math.e)
+    p0 = (3 * s + (1 - s)) / 4
+    assert st["balance_loss"] == pytest.approx(0.01 * 2 * (0.75 * p0 + 0.25 * (1 - p0)), abs=1e-15)
+
+
+def test_balance_loss_closed_forms():
+    # uniform shares and uniform probabilities (all logits equal): a * N * N * (1/N)(1/N) = a
+    for N in (4, 8, 128):
+        T = 2 * N
+        idx = np.array([[t % N] for t in range(T)])
+        st = O.routing_stats(np.zeros((T, N)), idx, np.bincount(idx.ravel(), minlength=N), alpha=0.01)
+        assert st["balance_loss"] == pytest.approx(0.01, abs=1e-15)
+    # every slot on expert 0: f = (1, 0, ..); the loss is a * N * mean probability of expert 0
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((30, 6))
+    p0 = np.mean([naive_softmax(list(row))[0] for row in z])
+    idx = np.zeros((30, 1), dtype=int)
+    st = O.routing_stats(z, idx, np.bincount(idx.ravel(), minlength=6), alpha=0.05)
+    assert st["balance_loss"] == pytest.approx(0.05 * 6 * p0, rel=1e-13)
+
+
+def test_reroute_rate_hand_worked_capacity():
+    # three tokens, both prefer expert 0, capacity 1, k = 1: token 0 keeps expert 0, token 1 moves
+    # to expert 1, token 2 finds no room (dropped): two of three slots re-routed
+    z = np.array([[2.0, 1.0]] * 3)
+    idx, _, fill = O.capacity_route(z, k=1, C=1)
+    assert idx.ravel().tolist() == [0, 1, -1] and fill.tolist() == [1, 1]
+    st = O.routing_stats(z, idx, fill)
+    assert st["reroute_rate"] == pytest.approx(2.0 / 3.0) and st["experts_touched"] == 2
