@@ -258,8 +258,8 @@ def forward(x, w_router, w_up, w_down, k: int, ffn: str, gating: str, w_gate=Non
     shared = (sh_gate, sh_up, sh_down) or None.
     tokens: evaluate the FFN/combine only for these tokens (routing always
     covers every token, since capacity couples them).
-    z: use these logits instead of computing step 1 (parity of the later
-    steps on the GPU's own logits).
+    z: use these logits instead of computing step 1 (logits the caller
+    already computed with router_logits, reused).
     Returns z, idx, w, counts, offsets, perm, inv, C, y (rows = tokens).
     """
     x = np.asarray(x)
@@ -326,14 +326,18 @@ def routing_stats(z, idx, counts, alpha: float = 0.01) -> Dict[str, object]:
     online calibration).  From [P3] (核心机制, the load-balancing loss): the
     value alpha * N * sum_i f_i * p_i, with f_i expert i's share of the routed
     slots and p_i its routing probability averaged over the tokens (softmax over
-    all N logits).  From [P5] §2.2 (expert capacity) and §3.3 (its re-route rate): the share of slots
-    that did not get their own ranked choice (slot j of a token not holding the
-    token's j-th ranked expert, a dropped slot included).
+    all N logits).  From [P5] §2.2 (expert capacity: a token whose choice is
+    full is sent on to its next-best expert) and §3.3 (the re-route rate it
+    monitors): the share of the T*k slots whose expert is not one of the
+    token's own k best-ranked experts, a dropped slot included.
 
-    Readings: shares are of the kept slots (the counts); empty experts add 0 to
+    Readings: a slot counts as re-routed by the expert it holds, not by its
+    position (the capacity passes fill slots in order, so a token can hold its
+    k best experts in another slot order); shares are of the kept slots (the counts); empty experts add 0 to
     the entropy; the standard deviation is the population one (over the N
     experts); ties among the three most used experts go to the lower id; with
-    fewer than three experts the missing ids are -1.
+    fewer than three experts the missing ids are -1; with no kept slot every
+    share-based value is NaN.  prob_mean is p_i for each expert.
     """
     z = _f64(z)
     idx = np.asarray(idx, dtype=np.int64)
@@ -341,21 +345,24 @@ def routing_stats(z, idx, counts, alpha: float = 0.01) -> Dict[str, object]:
     T, N = z.shape
     k = idx.shape[1]
     S = c.sum()
-    share = c / S
-    nz = share > 0
-    entropy = float(-(share[nz] * np.log2(share[nz])).sum())
+    nan = float("nan")
+    share = c / S if S > 0 else np.full(N, nan)
+    nz = c > 0
+    entropy = float(-(share[nz] * np.log2(share[nz])).sum()) if S > 0 else nan
     order = np.lexsort((np.arange(N), -c))              # count descending, then id ascending
     top = [int(e) for e in order[:3]] + [-1] * max(0, 3 - N)
-    top3_share = float(c[order[:3]].sum() / S)
+    top3_share = float(c[order[:3]].sum() / S) if S > 0 else nan
     mean = S / N
-    cv = float(math.sqrt(((c - mean) ** 2).mean()) / mean)
+    cv = float(math.sqrt(((c - mean) ** 2).mean()) / mean) if S > 0 else nan
     zm = z.max(axis=1, keepdims=True)
     p = np.exp(z - zm)
     p /= p.sum(axis=1, keepdims=True)
     p_mean = p.mean(axis=0)
     balance = float(alpha * N * (share * p_mean).sum())
     ranked = rank_experts(z)[:, :k]
-    rerouted = int((idx != ranked).sum())
+    own = (idx[:, :, None] == ranked[:, None, :]).any(axis=2)    # slot's expert in the top k
+    rerouted = int((~own).sum())
     return dict(entropy_bits=entropy, entropy_ideal_bits=math.log2(N), top3_share=top3_share,
                 max_share=float(share.max()), cv=cv, balance_loss=balance,
-                reroute_rate=rerouted / float(T * k), experts_touched=int((c > 0).sum()), top3=top)
+                reroute_rate=rerouted / float(T * k), experts_touched=int((c > 0).sum()), top3=top,
+                prob_mean=p_mean)

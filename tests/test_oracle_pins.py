@@ -440,6 +440,15 @@ def test_balance_loss_closed_forms():
     idx = np.zeros((30, 1), dtype=int)
     st = O.routing_stats(z, idx, np.bincount(idx.ravel(), minlength=6), alpha=0.05)
     assert st["balance_loss"] == pytest.approx(0.05 * 6 * p0, rel=1e-13)
+    # the mean probabilities are a distribution over the experts
+    assert st["prob_mean"].sum() == pytest.approx(1.0, abs=1e-15) and st["prob_mean"][0] == pytest.approx(p0)
+
+
+def test_routing_stats_no_kept_slot_is_undefined():
+    st = O.routing_stats(np.zeros((4, 5)), np.full((4, 2), -1), np.zeros(5, dtype=int))
+    for key in ("entropy_bits", "top3_share", "max_share", "cv", "balance_loss"):
+        assert math.isnan(st[key]), key
+    assert st["reroute_rate"] == 1.0 and st["experts_touched"] == 0 and st["top3"] == [0, 1, 2]
 
 
 def test_reroute_rate_hand_worked_capacity():
@@ -450,3 +459,15 @@ def test_reroute_rate_hand_worked_capacity():
     assert idx.ravel().tolist() == [0, 1, -1] and fill.tolist() == [1, 1]
     st = O.routing_stats(z, idx, fill)
     assert st["reroute_rate"] == pytest.approx(2.0 / 3.0) and st["experts_touched"] == 2
+
+
+def test_reroute_rate_counts_experts_not_slot_positions():
+    # two tokens ranking e0 > e1 > e2, k = 2, capacity 1.  First slots: token 0 takes e0, token 1
+    # finds e0 full and takes e1.  Second slots: token 0 finds e1 full and takes e2; token 1 finds
+    # e0 and e2 full (and holds e1): dropped.  Token 1's e1 is one of its two best experts, so of
+    # the four slots two are re-routed (token 0's e2 and token 1's dropped slot), not three.
+    z = np.array([[3.0, 2.0, 1.0]] * 2)
+    idx, _, fill = O.capacity_route(z, k=2, C=1)
+    assert idx.tolist() == [[0, 2], [1, -1]] and fill.tolist() == [1, 1, 1]
+    st = O.routing_stats(z, idx, fill)
+    assert st["reroute_rate"] == 0.5 and st["experts_touched"] == 3 and st["entropy_bits"] == pytest.approx(math.log2(3))
