@@ -44,6 +44,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self) -> int:
         ev = ctypes.c_void_p()
@@ -58,6 +59,11 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return float(ms.value)
+
+    def record(self, ev: int, stream: int) -> None:
+        rc = self.hip.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def destroy(self, ev: int) -> None:
         self.hip.hipEventDestroy(ev)
@@ -283,9 +289,29 @@ def main(argv=None) -> int:
     stage_ms = [sum(hip.elapsed_ms(ev[s], ev[s + 1]) for ev in events) / args.steps
                 for s in range(M.MOE_NUM_STAGES)]
     step_dev_ms = sum(hip.elapsed_ms(ev[0], ev[-1]) for ev in events) / args.steps
+    # Routing statistics of the same routing (outside the layer step): device time per call
+    # between two events around `steps` back-to-back calls.
+    st_out = None
+    ev_a, ev_b = hip.create(), hip.create()
+    layer.routing_stats(routing)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.record(ev_a, stream)
+    for _ in range(args.steps):
+        st_out = layer.routing_stats(routing)
+    hip.record(ev_b, stream)
+    torch.cuda.synchronize()
+    stats_us = hip.elapsed_ms(ev_a, ev_b) * 1e3 / args.steps
+    events.append([ev_a, ev_b])
     for ev in events + [list(p) for p in in_ev]:
         for e in ev:
             hip.destroy(e)
+    st_vals = st_out["stats"].cpu().numpy().tolist()
+    # algorithmic bytes: logits, indices and counts read once, the statistics written
+    st_bytes = cfg.T * cfg.N * 4 + cfg.T * cfg.k * 4 + cfg.N * 4 + M.MOE_NUM_STATS * 8 + 3 * 4
+    routing_stats = {"us_per_call": stats_us, "gbs": st_bytes / (stats_us * 1e-6) / 1e9,
+                     "values": dict(zip(M.STAT_NAMES, st_vals)),
+                     "top3": st_out["top3"].cpu().numpy().tolist()}
 
     counts = routing["counts"].cpu().numpy()
     alg = algorithmic_counts(cfg, counts)
@@ -326,6 +352,7 @@ def main(argv=None) -> int:
                   "hbm_frac": alg["bytes"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
                   "experts_touched": alg["touched"], "device_ms_per_step": step_dev_ms},
         "stages_ms": dict(zip(M.STAGE_NAMES, stage_ms)),
+        "routing_stats": routing_stats,
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -194,6 +194,35 @@ moe_status moe_layer_forward_timed(const moe_layer_desc *desc, const moe_weights
                                    void *ws, size_t ws_bytes, moe_stream_t stream,
                                    void *const *events);
 
+/* Number of values moe_routing_stats() writes to `stats`, in this order:
+ *   0 entropy_bits        -sum_i f_i log2 f_i over experts with f_i > 0, f_i = counts[i] / sum(counts)
+ *   1 entropy_ideal_bits  log2 N (every expert with the same share)
+ *   2 top3_share          share of the kept slots held by the three most used experts
+ *   3 max_share           largest f_i
+ *   4 cv                  population standard deviation of counts[0..N-1] over their mean
+ *   5 balance_loss        alpha * N * sum_i f_i * p_i, p_i = softmax over all N logits, averaged
+ *                         over the T tokens
+ *   6 reroute_rate        share of the T*k slots whose expert idx[t, j] is not among the token's
+ *                         k best-ranked experts (descending logit, ties to the lower id); dropped
+ *                         slots count
+ *   7 experts_touched     number of experts with counts[i] > 0 */
+#define MOE_NUM_STATS 8
+
+/* Routing health statistics of one call [P5 4.2 (entropy against log2 N, top-3 experts, std /
+ * mean of the counts), P3 MoE核心机制 (load-balancing loss alpha * N * sum f_i p_i), P5 2.2 and
+ * 3.3 (re-routing under capacity, its rate)].
+ *   logits [T, N] fp32, idx [T, k] int32 (-1 = dropped), counts [N] int32: the routing of one
+ *   call, e.g. moe_layer_forward's moe_routing outputs (counts must be those of idx).
+ *   alpha: balance-loss coefficient (the pages use 0.01).
+ *   stats [MOE_NUM_STATS] fp64 and top3 [3] int32 (the three most used experts, count
+ *   descending, ties to the lower id, -1 past N) out, on the device; prob_mean [N] fp64 out
+ *   (p_i above) or NULL.  If no slot is kept (counts all 0) the share-based values 0, 2-5 are NaN.
+ *   ws/ws_bytes: workspace of at least moe_workspace_size(desc) bytes (per-block partial sums).
+ *   Deterministic: the same inputs give the same bits.  T must be >= 1. */
+moe_status moe_routing_stats(const moe_layer_desc *desc, const float *logits, const int32_t *idx,
+                             const int32_t *counts, double alpha, double *stats, int32_t *top3,
+                             double *prob_mean, void *ws, size_t ws_bytes, moe_stream_t stream);
+
 /* Static text of a status code. */
 const char *moe_status_str(moe_status s);
 /* Detail of the last error on the calling thread ("" if none). */

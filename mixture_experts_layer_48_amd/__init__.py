@@ -21,6 +21,9 @@ MOE_GATE_TOPK_SOFTMAX, MOE_GATE_SOFTMAX_TOPK = 0, 1
 MOE_FFN_RELU2, MOE_FFN_SWIGLU = 0, 1
 MOE_NUM_STAGES = 6
 STAGE_NAMES = ("route", "capacity", "permute", "ffn_in", "ffn_out", "combine")
+MOE_NUM_STATS = 8
+STAT_NAMES = ("entropy_bits", "entropy_ideal_bits", "top3_share", "max_share", "cv", "balance_loss",
+              "reroute_rate", "experts_touched")
 
 _DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16}
 _FFNS = {"relu2": MOE_FFN_RELU2, "swiglu": MOE_FFN_SWIGLU}
@@ -80,8 +83,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.POINTER(moe_routing), vp, sz, vp]
     lib.moe_layer_forward_timed.argtypes = [pdesc, ctypes.POINTER(moe_weights), vp, vp,
                                             ctypes.POINTER(moe_routing), vp, sz, vp, ctypes.POINTER(vp)]
+    lib.moe_routing_stats.argtypes = [pdesc, vp, vp, vp, ctypes.c_double, vp, vp, vp, vp, sz, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-              "moe_layer_forward_timed"):
+              "moe_layer_forward_timed", "moe_routing_stats"):
         getattr(lib, f).restype = i32
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -173,6 +177,14 @@ def moe_layer_forward(desc, weights: Dict, x, y, routing: Optional[Dict] = None,
         _check(st, "moe_layer_forward_timed")
 
 
+def moe_routing_stats(desc, logits, idx, counts, stats, top3, ws, alpha: float = 0.01, prob_mean=None,
+                      stream=None) -> None:
+    _check(load_library().moe_routing_stats(ctypes.byref(desc), _ptr(logits), _ptr(idx), _ptr(counts),
+                                            float(alpha), _ptr(stats), _ptr(top3), _ptr(prob_mean), _ptr(ws),
+                                            0 if ws is None else ws.numel() * ws.element_size(),
+                                            _stream(stream)), "moe_routing_stats")
+
+
 # ---------------------------------------------------------------- convenience
 class MoELayer:
     """One layer's descriptor, weights (device tensors in the ABI layouts) and workspace.
@@ -204,6 +216,18 @@ class MoELayer:
                     offsets=torch.empty(N + 1, dtype=torch.int32, device=dev),
                     perm=torch.empty(T * k, dtype=torch.int32, device=dev),
                     inv=torch.empty(T * k, dtype=torch.int32, device=dev))
+
+    def routing_stats(self, r: Dict, alpha: float = 0.01, with_prob_mean: bool = False) -> Dict:
+        """Enqueue moe_routing_stats on the routing tensors `r` of a forward(routing=True) call;
+        returns device tensors stats [MOE_NUM_STATS] fp64, top3 [3] int32 (and prob_mean [N])."""
+        import torch
+        out = dict(stats=torch.empty(MOE_NUM_STATS, dtype=torch.float64, device=self.device),
+                   top3=torch.empty(3, dtype=torch.int32, device=self.device))
+        if with_prob_mean:
+            out["prob_mean"] = torch.empty(self.desc.N, dtype=torch.float64, device=self.device)
+        moe_routing_stats(self.desc, r["logits"], r["idx"], r["counts"], out["stats"], out["top3"], self.ws,
+                          alpha=alpha, prob_mean=out.get("prob_mean"))
+        return out
 
     def forward(self, x, routing: bool = False, y=None, out_routing: Optional[Dict] = None, events=None):
         import torch

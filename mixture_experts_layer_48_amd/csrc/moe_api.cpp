@@ -101,7 +101,8 @@ Layout layout_of(const moe_layer_desc& d) {
                            align256(router_workspace_bytes(d.T, d.d, d.N, d.dtype)));
     // fp32 expert rows, one copy per K part of the out-projection
     L.yp = o; o += align256((size_t)rows_total(d) * d.d * 4 * ksplit_of(d));
-    L.total = o;
+    // moe_routing_stats() reuses the workspace from offset 0 for its partial sums
+    L.total = std::max(o, align256(stats_workspace_bytes(d.T, d.N)));
     return L;
 }
 size_t route_ws_bytes(const moe_layer_desc& d, bool have_logits) {
@@ -292,6 +293,25 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_weights
 moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_weights* weights, const void* x, void* y,
                              const moe_routing* routing, void* ws, size_t ws_bytes, moe_stream_t stream) {
     return moe_layer_forward_timed(desc, weights, x, y, routing, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_routing_stats(const moe_layer_desc* desc, const float* logits, const int32_t* idx,
+                             const int32_t* counts, double alpha, double* stats, int32_t* top3, double* prob_mean,
+                             void* ws, size_t ws_bytes, moe_stream_t stream) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const moe_layer_desc& d = *desc;
+    if (d.T < 1) return fail(MOE_ERR_INVALID_ARG, "routing statistics need T >= 1");
+    if (!logits || !idx || !counts || !stats || !top3)
+        return fail(MOE_ERR_INVALID_ARG, "logits, idx, counts, stats and top3 are required");
+    if (std::isnan(alpha) || std::isinf(alpha)) return fail(MOE_ERR_INVALID_ARG, "alpha must be finite");
+    const size_t need = stats_workspace_bytes(d.T, d.N);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace too small for moe_routing_stats: need " + std::to_string(need));
+    hipError_t e = launch_routing_stats(logits, idx, counts, d.T, d.N, d.k, alpha, ws, stats, top3, prob_mean,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "routing statistics launch");
 }
 
 const char* moe_status_str(moe_status s) {

@@ -43,3 +43,9 @@ hipError_t launch_ffn_in(const FfnLaunch& a, hipStream_t s);   // H = act(x W_in
 hipError_t launch_ffn_out(const FfnLaunch& a, hipStream_t s);  // y_perm = scale * H W_out
 hipError_t launch_combine(const void* y_perm, const int32_t* inv, const float* w, void* y, int T,
                           int k, int d, int has_shared, int dtype, int nparts, hipStream_t s);
+
+// Routing statistics: workspace of per-block partial sums, then the two-kernel launch.
+size_t stats_workspace_bytes(int T, int N);
+hipError_t launch_routing_stats(const float* z, const int32_t* idx, const int32_t* counts, int T, int N, int k,
+                                double alpha, void* ws, double* stats, int32_t* top3, double* prob_mean,
+                                hipStream_t s);

@@ -128,6 +128,30 @@ def test_missing_pointers_and_small_workspace(lib):
                                        need, None, events) == M.MOE_ERR_INVALID_ARG
 
 
+def test_routing_stats_argument_errors(lib):
+    desc = _desc(T=300, N=64, k=4)
+    need = M.moe_workspace_size(desc)
+    call = lambda d, z, i, c, alpha, st, t3, ws, nb: lib.moe_routing_stats(  # noqa: E731
+        ctypes.byref(d), z, i, c, alpha, st, t3, None, ws, nb, None)
+    assert call(desc, None, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, need) == M.MOE_ERR_INVALID_ARG
+    assert call(desc, FAKE, FAKE, FAKE, 0.01, FAKE, None, FAKE, need) == M.MOE_ERR_INVALID_ARG
+    assert call(desc, FAKE, FAKE, FAKE, float("inf"), FAKE, FAKE, FAKE, need) == M.MOE_ERR_INVALID_ARG
+    assert call(_desc(T=0), FAKE, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, need) == M.MOE_ERR_INVALID_ARG
+    assert call(desc, FAKE, FAKE, FAKE, 0.01, FAKE, FAKE, None, need) == M.MOE_ERR_WORKSPACE
+    assert call(desc, FAKE, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, 64) == M.MOE_ERR_WORKSPACE
+    assert call(_desc(k=0), FAKE, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, need) == M.MOE_ERR_INVALID_ARG
+    assert b"workspace" in lib.moe_last_error() or b"k must" in lib.moe_last_error()
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define MOE_NUM_STATS (\d+)", text).group(1)) == M.MOE_NUM_STATS == len(M.STAT_NAMES)
+    assert int(re.search(r"#define MOE_NUM_STAGES (\d+)", text).group(1)) == M.MOE_NUM_STAGES
+    block = text[text.index("#define MOE_NUM_STATS") - 1200:text.index("#define MOE_NUM_STATS")]
+    listed = re.findall(r"\*\s+\d\s+([a-z0-9_]+)", block)
+    assert tuple(listed) == M.STAT_NAMES
+
+
 def test_empty_batch_is_a_no_op(lib):
     desc = _desc(T=0)
     good = M.moe_weights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)

@@ -1,15 +1,22 @@
 """GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
 
-Layered checks (routing is integer work decided by floating point, so it is
-checked on identical logits first):
-  P-a  the GPU's top-k / capacity indices, gate weights, counts, offsets, perm
-       and inv equal the oracle's steps 2-4 run on the GPU's own fp32 logits
-       (bit-exact integers, weights within 1e-6);
-  P-b  the GPU routing equals the oracle's routing from float64 logits except
-       on near-tie tokens (adjacent deciding logits closer than 1e-6), which are
-       counted and printed;
-  P-c  y matches the oracle run on the same routing: max |err| / RMS(y) within
-       1e-4 (fp32 layers) or 2e-2 (bf16 layers).
+Layered checks.  The oracle only ever sees the seeded inputs, never a value the
+GPU computed.  Routing is integer work decided by floating point:
+  P-a  exact logits: with a selection router (router rows are unit vectors and
+       the selected inputs lie on a coarse grid, so every logit is exact in any
+       summation order, with many exact ties) the GPU's logits, top-k /
+       capacity indices, counts, offsets, perm and inv equal the oracle's bit
+       for bit, and the gate weights agree within 1e-6;
+  P-b  random routers: the GPU logits are within the error bound of their fp32
+       chunked accumulation, the grouping is the stable grouping of the GPU's
+       own indices (properties), and the routing equals the oracle's from its
+       float64 logits except on near-tie tokens (adjacent deciding logits
+       closer than 1e-6), which are counted and printed;
+  P-c  y matches the oracle's forward on its own routing, on every token routed
+       alike: max |err| / RMS(y) within 1e-4 (fp32 layers) or 2e-2 (bf16
+       layers), plus half an ulp of the output format;
+  P-d  routing statistics of the GPU's routing against the oracle's statistics
+       of its own routing.
 Small cases run the oracle on every token and span several tiles with ragged
 tails; the full-size layers check every token's routing and a sample of
 tokens' outputs.
@@ -23,8 +30,8 @@ import torch
 import mixture_experts_layer_48_amd as M
 import oracle as O
 import workloads as W
-from gpu_harness import (check_routing_exact_on_gpu_logits, check_routing_vs_fp64, check_y, f64, log,
-                         oracle_forward, rel_rms_err, routing_to_np, run_layer, desc_of)
+from gpu_harness import (check_routing, check_stats, check_y, f64, gpu_routing_stats, log, oracle_forward,
+                         rel_rms_err, routing_to_np, run_layer, desc_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,15 +103,28 @@ def _free():
     torch.cuda.empty_cache()
 
 
+def _stats_parity(cfg, layer, r, rn, z64, zerr, ref):
+    g = gpu_routing_stats(layer, r)
+    o = O.routing_stats(z64, ref["idx"], ref["counts"])
+    slack = len(O.near_tie_tokens(z64, cfg.k, max(1e-6, 2.0 * zerr))) * cfg.k
+    if not np.array_equal(rn["idx"], ref["idx"]):
+        # counts differ where near-tie tokens went elsewhere: the count-based values are only
+        # logged then
+        log(f"[{cfg.name}] routing differs on near ties: statistics not compared")
+        return g
+    check_stats(cfg, g, o, zerr=zerr, reroute_slack=slack)
+    return g
+
+
 def _full_parity(cfg, inp):
     log(f"[{cfg.name}] T={cfg.T} d={cfg.d} N={cfg.N} k={cfg.k} d_ff={cfg.d_ff} {cfg.dtype} {cfg.ffn} "
         f"{cfg.gating} cf={cfg.capacity_factor} shared={cfg.has_shared}")
     layer, y, r = run_layer(cfg, inp)
     rn = routing_to_np(r)
-    check_routing_exact_on_gpu_logits(cfg, rn)
-    check_routing_vs_fp64(cfg, inp, rn)
-    ref = oracle_forward(cfg, inp, z=rn["logits"].astype(np.float64))
-    check_y(cfg, f64(y), ref["y"])
+    z64, zerr, alike = check_routing(cfg, inp, rn)
+    ref = oracle_forward(cfg, inp, z=z64)
+    check_y(cfg, f64(y)[alike], ref["y"][alike], label=f" {int(alike.sum())} of {cfg.T} tokens:")
+    _stats_parity(cfg, layer, r, rn, z64, zerr, ref)
     return layer, y, r
 
 
@@ -192,17 +212,18 @@ def test_full_size_layer(name):
     inp = W.make_inputs(cfg, "cuda")
     layer, y, r = run_layer(cfg, inp)
     rn = routing_to_np(r)
-    check_routing_exact_on_gpu_logits(cfg, rn)
-    log(f"[{name}] routing on GPU logits: exact")
-    check_routing_vs_fp64(cfg, inp, rn)
+    z64, zerr, alike = check_routing(cfg, inp, rn)
     rng = np.random.default_rng(cfg.seed)
-    tokens = np.sort(rng.choice(cfg.T, size=min(SAMPLE_TOKENS[name], cfg.T), replace=False))
-    ref = oracle_forward(cfg, inp, tokens=tokens, z=rn["logits"].astype(np.float64))
+    pool = np.nonzero(alike)[0]
+    tokens = np.sort(rng.choice(pool, size=min(SAMPLE_TOKENS[name], pool.size), replace=False))
+    ref = oracle_forward(cfg, inp, tokens=tokens, z=z64)
     check_y(cfg, f64(y)[tokens], ref["y"], label=f" sampled tokens {tokens.tolist()}:")
+    _stats_parity(cfg, layer, r, rn, z64, zerr, ref)
     if cfg.capacity_factor > 0:
         C_ = O.expert_capacity(cfg.capacity_factor, cfg.T, cfg.k, cfg.N)
         assert rn["counts"].max() <= C_ and rn["counts"].sum() == cfg.T * cfg.k
         log(f"[{name}] capacity {C_}: experts full = {int((rn['counts'] == C_).sum())}, "
-            f"slots re-routed = {int((rn['idx'] != O.rank_experts(rn['logits'])[:, :cfg.k]).sum())}")
+            f"slots outside their token's top {cfg.k} = "
+            f"{int((~(ref['idx'][:, :, None] == O.rank_experts(z64)[:, None, :cfg.k]).any(2)).sum())}")
     del layer, y, r, inp
     _free()

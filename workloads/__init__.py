@@ -50,6 +50,7 @@ import torch
 # tensor streams (one generator stream per tensor)
 STREAM_X, STREAM_ROUTER, STREAM_GATE, STREAM_UP, STREAM_DOWN = 1, 2, 3, 4, 5
 STREAM_SH_GATE, STREAM_SH_UP, STREAM_SH_DOWN = 6, 7, 8
+STREAM_GRID, STREAM_GRID_BIAS, STREAM_LOGITS = 9, 10, 11
 
 FFN_RELU2 = "relu2"
 FFN_SWIGLU = "swiglu"
@@ -170,6 +171,41 @@ def make_inputs(cfg: LayerConfig, device="cpu", experts: Optional[range] = None)
     else:
         out["sh_gate"] = out["sh_up"] = out["sh_down"] = None
     return out
+
+
+def make_selection_router_inputs(cfg: LayerConfig, device="cpu", levels: int = 16,
+                                 grid_bias: bool = False) -> Dict[str, torch.Tensor]:
+    """Inputs of one layer call whose router logits are exact in any summation order.
+
+    As make_inputs, except: row e of w_router is the unit vector on input feature e, so that
+    logit z[t, e] is x[t, e] itself; x[t, :N] takes values k/8 for integer k drawn uniformly
+    from [-levels/2, levels/2) (few distinct values: many exactly tied logits); with
+    grid_bias, logit_bias[e] is a multiple of 1/4 in [-1, 1] (the sum with x stays exact in
+    fp32).  Needs d >= N."""
+    if cfg.d < cfg.N:
+        raise ValueError("a selection router needs d >= N")
+    device = torch.device(device)
+    out = make_inputs(cfg, device)
+    g = _gen(device, cfg.seed, STREAM_GRID)
+    steps = torch.randint(-(levels // 2), levels - levels // 2, (cfg.T, cfg.N), generator=g, device=device)
+    out["x"][:, :cfg.N] = (steps.float() / 8.0).to(out["x"].dtype)
+    wr = torch.zeros((cfg.N, cfg.d), dtype=out["x"].dtype, device=device)
+    wr[torch.arange(cfg.N, device=device), torch.arange(cfg.N, device=device)] = 1.0
+    out["w_router"] = wr
+    if grid_bias:
+        gb = _gen(device, cfg.seed, STREAM_GRID_BIAS)
+        out["logit_bias"] = torch.randint(-4, 5, (cfg.N,), generator=gb, device=device).float() / 4.0
+    return out
+
+
+def make_logits(T: int, N: int, seed: int, device="cpu", levels: Optional[int] = None) -> torch.Tensor:
+    """Router logits [T, N] fp32 for the routing-statistics cases: N(0, 1) draws, or with
+    `levels`, values k/8 for integer k uniform in [-levels/2, levels/2) (exact ties)."""
+    device = torch.device(device)
+    g = _gen(device, seed, STREAM_LOGITS)
+    if levels is None:
+        return torch.randn((T, N), generator=g, device=device, dtype=torch.float32)
+    return torch.randint(-(levels // 2), levels - levels // 2, (T, N), generator=g, device=device).float() / 8.0
 
 
 def scaled(cfg: LayerConfig, **kw) -> LayerConfig:
