@@ -24,6 +24,8 @@ The layer (one GPU's whole expert set, no cross-device step):
   5. expert FFN on each expert's rows               [P1 什麼是 MoE 模型: two linear maps + activation]
   6. shared expert on every token (optional)        [P4 专家粒度; P3 DeepSeek-V4 架构细节]
   7. gate-weighted combine                          [P1 動態 token 路由 step 6; P2 代码]
+Beside the layer: routing statistics [P5 §4.2, §2.2/§3.3; P3 核心机制] and the
+send / receive layouts of expert parallelism [P1 專家平行化詳解, 動態 token 路由].
 
 Readings taken where the pages leave a step open (each also listed in the
 design notes): equal logits rank the lower expert id first; slot 0 is the
@@ -56,6 +58,7 @@ __all__ = [
     "router_logits", "rank_experts", "gate_weights", "topk_route", "expert_capacity",
     "capacity_route", "route_from_logits", "group_by_expert", "silu", "expert_ffn",
     "combine", "forward", "param_counts", "near_tie_tokens", "routing_stats",
+    "ep_dispatch_layout", "ep_receive_layout",
 ]
 
 
@@ -287,6 +290,76 @@ def forward(x, w_router, w_up, w_down, k: int, ffn: str, gating: str, w_gate=Non
     y = combine(slot_out, w[tok], y_sh)
     return dict(z=z, idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, C=C, y=y,
                 y_shared=y_sh)
+
+
+# ---------------------------------------------------------------- expert parallelism
+def ep_dispatch_layout(idx, owner: Sequence[int], G: int) -> Dict[str, np.ndarray]:
+    """Send-side layout when the experts are spread over G ranks ([P1]
+    專家平行化詳解: each GPU owns some experts; 動態 token 路由 steps 3-4:
+    every token goes to the GPUs that own its experts).
+
+    owner[e] = rank holding expert e.  Slot s = t*k + j is kept iff its
+    expert e = idx[t, j] lies in [0, N).  Kept slots are ordered by the key
+    (owner[e], e, s): rank r's rows come out contiguous, and inside them each
+    expert's rows in slot order.  Returns counts [N]; expert_offsets [N+1]
+    (row of expert e's first slot = kept slots with a smaller (owner, expert)
+    key; [N] = kept slots); send_counts [G]; send_offsets [G+1]; perm (row ->
+    slot); inv (slot -> row, -1 if dropped).
+    """
+    flat = [int(e) for e in np.asarray(idx).reshape(-1)]
+    N = len(owner)
+    kept = [s for s, e in enumerate(flat) if 0 <= e < N]
+    order = sorted(kept, key=lambda s: (owner[flat[s]], flat[s], s))
+    perm = np.array(order, dtype=np.int64)
+    inv = np.full(len(flat), -1, dtype=np.int64)
+    for r, s in enumerate(order):
+        inv[s] = r
+    counts = np.zeros(N, dtype=np.int64)
+    for s in kept:
+        counts[flat[s]] += 1
+    expert_offsets = np.zeros(N + 1, dtype=np.int64)
+    for e in range(N):
+        expert_offsets[e] = sum(int(counts[e2]) for e2 in range(N) if (owner[e2], e2) < (owner[e], e))
+    expert_offsets[N] = len(kept)
+    send_counts = np.zeros(G, dtype=np.int64)
+    for s in kept:
+        send_counts[owner[flat[s]]] += 1
+    send_offsets = np.zeros(G + 1, dtype=np.int64)
+    for r in range(G):
+        send_offsets[r + 1] = send_offsets[r] + send_counts[r]
+    return dict(counts=counts, expert_offsets=expert_offsets, send_counts=send_counts,
+                send_offsets=send_offsets, perm=perm, inv=inv)
+
+
+def ep_receive_layout(recv_counts, owner: Sequence[int], rank: int) -> Dict[str, np.ndarray]:
+    """Receive-side layout on rank `rank` ([P1] 動態 token 路由 steps 3-5).
+
+    recv_counts[s][e] = rows source s sends for expert e.  The receive buffer
+    holds the sources in order; inside source s's block, this rank's experts
+    in ascending id, each with its recv_counts[s][e] rows.  The grouped order
+    that the experts run on takes local expert by local expert (ascending
+    id), and inside one expert the sources in order, each source's rows in
+    its order.  Returns recv_offsets [G+1] (first receive row of each
+    source), local_offsets [n_local+1], recv_perm (grouped row -> receive
+    row), recv_inv (receive row -> grouped row).
+    """
+    rc = np.asarray(recv_counts, dtype=np.int64)
+    G, N = rc.shape
+    local = [e for e in range(N) if owner[e] == rank]
+    rows = [(s, e, i) for s in range(G) for e in local for i in range(int(rc[s, e]))]
+    grouped = sorted(range(len(rows)), key=lambda r: (local.index(rows[r][1]), rows[r][0], rows[r][2]))
+    recv_perm = np.array(grouped, dtype=np.int64)
+    recv_inv = np.zeros(len(rows), dtype=np.int64)
+    for g, r in enumerate(grouped):
+        recv_inv[r] = g
+    recv_offsets = np.zeros(G + 1, dtype=np.int64)
+    for s in range(G):
+        recv_offsets[s + 1] = recv_offsets[s] + sum(int(rc[s, e]) for e in local)
+    local_offsets = np.zeros(len(local) + 1, dtype=np.int64)
+    for le, e in enumerate(local):
+        local_offsets[le + 1] = local_offsets[le] + int(rc[:, e].sum())
+    return dict(recv_offsets=recv_offsets, local_offsets=local_offsets, recv_perm=recv_perm,
+                recv_inv=recv_inv, local_experts=np.array(local, dtype=np.int64))
 
 
 # ---------------------------------------------------------------- counting

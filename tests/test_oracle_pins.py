@@ -471,3 +471,88 @@ def test_reroute_rate_counts_experts_not_slot_positions():
     assert idx.tolist() == [[0, 2], [1, -1]] and fill.tolist() == [1, 1, 1]
     st = O.routing_stats(z, idx, fill)
     assert st["reroute_rate"] == 0.5 and st["experts_touched"] == 3 and st["entropy_bits"] == pytest.approx(math.log2(3))
+
+
+# ---------------------------------------------------------------- expert parallelism layouts
+def test_ep_dispatch_one_rank_is_the_grouping_by_expert():
+    rng = np.random.default_rng(21)
+    idx = rng.integers(-1, 6, size=(40, 3))
+    a = O.ep_dispatch_layout(idx, [0] * 6, 1)
+    counts, offsets, perm, inv = O.group_by_expert(idx, 6)
+    assert np.array_equal(a["perm"], perm) and np.array_equal(a["inv"], inv)
+    assert np.array_equal(a["counts"], counts) and np.array_equal(a["expert_offsets"], offsets)
+    assert a["send_counts"].tolist() == [offsets[-1]] and a["send_offsets"].tolist() == [0, offsets[-1]]
+
+
+def test_ep_dispatch_contiguous_owners_keep_expert_order():
+    # ranks owning contiguous expert blocks: destination-major order is expert-major order
+    rng = np.random.default_rng(22)
+    idx = rng.integers(0, 8, size=(50, 2))
+    owner = [e // 2 for e in range(8)]
+    a = O.ep_dispatch_layout(idx, owner, 4)
+    counts, offsets, perm, inv = O.group_by_expert(idx, 8)
+    assert np.array_equal(a["perm"], perm)
+    assert a["send_counts"].tolist() == [int(counts[2 * r] + counts[2 * r + 1]) for r in range(4)]
+
+
+def test_ep_dispatch_hand_worked_interleaved_owners():
+    # T=3, k=2, N=4, G=2, rank 0 owns experts 0 and 2, rank 1 owns 1 and 3.
+    # slots: s0->e1, s1->e0, s2->e2, s3->e3, s4->e0, s5->e1.  Rank 0's rows: e0 (s1, s4), e2 (s2);
+    # rank 1's rows: e1 (s0, s5), e3 (s3).
+    idx = np.array([[1, 0], [2, 3], [0, 1]])
+    a = O.ep_dispatch_layout(idx, [0, 1, 0, 1], 2)
+    assert a["perm"].tolist() == [1, 4, 2, 0, 5, 3]
+    assert a["inv"].tolist() == [3, 0, 2, 5, 1, 4]
+    assert a["send_counts"].tolist() == [3, 3] and a["send_offsets"].tolist() == [0, 3, 6]
+    assert a["counts"].tolist() == [2, 2, 1, 1] and a["expert_offsets"].tolist() == [0, 3, 2, 5, 6]
+
+
+def test_ep_receive_hand_worked():
+    # rank 0 owns experts 0 and 2 of 4; source 0 sends 2 rows for e0 and 1 for e2, source 1 sends
+    # 1 for e0 and 3 for e2.  Receive rows: s0: e0 e0 e2 | s1: e0 e2 e2 e2.  Grouped: e0 from s0
+    # (rows 0, 1) and s1 (row 3), then e2 from s0 (row 2) and s1 (rows 4-6).
+    rc = np.array([[2, 9, 1, 9], [1, 9, 3, 9]])
+    b = O.ep_receive_layout(rc, [0, 1, 0, 1], 0)
+    assert b["recv_perm"].tolist() == [0, 1, 3, 2, 4, 5, 6]
+    assert b["recv_inv"].tolist() == [0, 1, 3, 2, 4, 5, 6]
+    assert b["local_offsets"].tolist() == [0, 3, 7] and b["recv_offsets"].tolist() == [0, 3, 7]
+    assert b["local_experts"].tolist() == [0, 2]
+
+
+def test_ep_round_trip_brute_force():
+    # G sources with their own routings; simulate both exchanges.  Each rank's grouped rows for
+    # a local expert must be exactly the (source, slot) pairs routed to it, in (source, slot)
+    # order, and every slot's output must come back to the row its source's inv names.
+    rng = np.random.default_rng(23)
+    N, G, k = 7, 3, 2
+    owner = [int(v) for v in rng.integers(0, G, size=N)]
+    owner[0], owner[1], owner[2] = 0, 1, 2
+    srcs = [rng.integers(-1, N, size=(int(rng.integers(1, 12)), k)) for _ in range(G)]
+    disp = [O.ep_dispatch_layout(i, owner, G) for i in srcs]
+    # what each source sends: its send rows, tagged (source, slot)
+    send = [[(s, int(d["perm"][r])) for r in range(len(d["perm"]))] for s, d in enumerate(disp)]
+    recv_counts = np.array([d["counts"] for d in disp])
+    back = [dict() for _ in range(G)]
+    for r in range(G):
+        recv = [row for s in range(G) for row in send[s][disp[s]["send_offsets"][r]:disp[s]["send_offsets"][r + 1]]]
+        b = O.ep_receive_layout(recv_counts, owner, r)
+        assert b["recv_offsets"][-1] == len(recv)
+        grouped = [recv[i] for i in b["recv_perm"]]
+        for le, e in enumerate(b["local_experts"]):
+            rows = grouped[b["local_offsets"][le]:b["local_offsets"][le + 1]]
+            want = [(s, t * k + j) for s in range(G) for t in range(srcs[s].shape[0]) for j in range(k)
+                    if srcs[s][t, j] == e]
+            assert rows == want
+        # expert "outputs" = the grouped rows' tags; unpack into receive order, return by source
+        ret = [grouped[b["recv_inv"][i]] for i in range(len(recv))]
+        assert ret == recv
+        for s in range(G):
+            back[s][r] = ret[b["recv_offsets"][s]:b["recv_offsets"][s + 1]]
+    for s in range(G):
+        returned = [row for r in range(G) for row in back[s][r]]     # rank order = send order
+        flat = srcs[s].reshape(-1)
+        for slot in range(flat.size):
+            if 0 <= flat[slot] < N:
+                assert returned[disp[s]["inv"][slot]] == (s, slot)
+            else:
+                assert disp[s]["inv"][slot] == -1
