@@ -217,6 +217,55 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
                       f"{dt:.1f} s including the float64 conversion of each touched expert's weights"}
 
 
+def ep_layout_timing(M, cfg, desc, inp, routing, hip, steps: int, G: int = 8):
+    """Device time of the expert-parallel layouts for one rank of a G-way placement (contiguous
+    expert blocks; this batch's routing as every source's): send layout + packing of the rows,
+    receive layout of rank 0 (G copies of the counts), and the unpack of its expert outputs.
+    Outside the layer step; bytes are the rows moved (read + write)."""
+    import torch
+    G = min(G, cfg.N)
+    owner = [e * G // cfg.N for e in range(cfg.N)]
+    T, k, N, d = cfg.T, cfg.k, cfg.N, cfg.d
+    i32 = dict(dtype=torch.int32, device="cuda")
+    outs = [torch.empty(n, **i32) for n in (N, N + 1, G, G + 1, T * k, T * k)]
+    send_buf = torch.empty((T * k, d), dtype=cfg.torch_dtype, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = hip.create(), hip.create()
+        hip.record(a, stream)
+        for _ in range(steps):
+            fn()
+        hip.record(b, stream)
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(a, b) * 1e3 / steps
+        hip.destroy(a)
+        hip.destroy(b)
+        return us
+
+    disp = lambda: M.moe_ep_dispatch(desc, routing["idx"], owner, G, *outs, inp["x"], send_buf)  # noqa: E731
+    dispatch_us = timed(disp)
+    layout_us = timed(lambda: M.moe_ep_dispatch(desc, routing["idx"], owner, G, *outs))
+    kept = int(outs[3][G].item())
+    rc = outs[0].repeat(G).view(G, N).contiguous()
+    R = int(rc[:, [e for e in range(N) if owner[e] == 0]].sum().item())
+    nl = sum(1 for e in range(N) if owner[e] == 0)
+    ro, lo = torch.empty(G + 1, **i32), torch.empty(nl + 1, **i32)
+    rp, ri = torch.empty(max(R, 1), **i32), torch.empty(max(R, 1), **i32)
+    recv_us = timed(lambda: M.moe_ep_receive_layout(N, G, owner, 0, rc, R, ro, lo, rp, ri))
+    yg = torch.empty((max(R, 1), d), dtype=torch.float32, device="cuda")
+    ret = torch.empty_like(yg)
+    unpack_us = timed(lambda: M.moe_ep_unpack(G, R, d * 4, ro, ri, yg, ret))
+    eb = cfg.elem_bytes
+    return {"G": G, "owner": "contiguous", "rows_sent": kept, "rows_received_rank0": R,
+            "dispatch_and_pack_us": dispatch_us, "dispatch_layout_us": layout_us,
+            "pack_gbs": 2 * kept * d * eb / max(dispatch_us - layout_us, 1e-3) / 1e3,
+            "receive_layout_us": recv_us, "unpack_us": unpack_us,
+            "unpack_gbs": 2 * R * d * 4 / max(unpack_us, 1e-3) / 1e3}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +355,7 @@ def main(argv=None) -> int:
     for ev in events + [list(p) for p in in_ev]:
         for e in ev:
             hip.destroy(e)
+    ep_layout = ep_layout_timing(M, cfg, desc, inp, routing, hip, args.steps)
     st_vals = st_out["stats"].cpu().numpy().tolist()
     # algorithmic bytes: logits, indices and counts read once, the statistics written
     st_bytes = cfg.T * cfg.N * 4 + cfg.T * cfg.k * 4 + cfg.N * 4 + M.MOE_NUM_STATS * 8 + 3 * 4
@@ -353,6 +403,7 @@ def main(argv=None) -> int:
                   "experts_touched": alg["touched"], "device_ms_per_step": step_dev_ms},
         "stages_ms": dict(zip(M.STAGE_NAMES, stage_ms)),
         "routing_stats": routing_stats,
+        "ep_layout": ep_layout,
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -223,6 +223,58 @@ moe_status moe_routing_stats(const moe_layer_desc *desc, const float *logits, co
                              const int32_t *counts, double alpha, double *stats, int32_t *top3,
                              double *prob_mean, void *ws, size_t ws_bytes, moe_stream_t stream);
 
+/* ---- Expert parallelism: the layouts either side of the two all-to-alls [P1 專家平行化詳解 (each
+ * GPU owns a subset of the experts; two all-to-alls per layer), P1 動態 token 路由 steps 3-6 (tokens
+ * go to the GPUs owning their experts, the outputs come back, the combine runs at the origin)].
+ * The exchanges themselves (counts, then rows, then the rows back) belong to the caller's
+ * collective library; these calls produce and consume the buffers they carry.
+ * owner: HOST array [N], owner[e] = rank holding expert e, each in [0, G); 1 <= G <= MOE_EP_MAX_RANKS.
+ * A rank's local experts are the experts it owns, in ascending id (its weight stacks in that order). */
+#define MOE_EP_MAX_RANKS 64
+
+/* Send side, on each source rank: the stable grouping of its T*k slots by (owner rank, expert),
+ * so that destination r's rows are the contiguous range send_offsets[r] .. send_offsets[r+1]-1
+ * and, inside it, each expert's rows are contiguous in ascending slot order.
+ *   idx [T, k] in (-1 or an index outside [0, N) = dropped slot).
+ *   counts [N], expert_offsets [N + 1] (first send row of expert e; [N] = kept slots),
+ *   send_counts [G], send_offsets [G + 1], perm [T * k] (send row -> slot), inv [T * k] (slot ->
+ *   send row, -1 if dropped): outputs, required.  counts is what the count exchange sends to
+ *   every destination.
+ *   x [T, d] and send_buf [T * k, d] (layer dtype): optional (both or neither); send row r
+ *   receives x[perm[r] / k]. */
+moe_status moe_ep_dispatch(const moe_layer_desc *desc, const int32_t *idx, const int32_t *owner, int32_t G,
+                           int32_t *counts, int32_t *expert_offsets, int32_t *send_counts,
+                           int32_t *send_offsets, int32_t *perm, int32_t *inv, const void *x,
+                           void *send_buf, moe_stream_t stream);
+
+/* Receive side, on rank `rank`: the layout of the rows the sources sent it.
+ *   recv_counts [G, N] int32 device: row s = source s's counts (from moe_ep_dispatch).
+ *   The receive buffer is source-major: source s's rows are recv_offsets[s] ..
+ *   recv_offsets[s+1]-1, ordered as that source sent them.
+ *   Outputs: recv_offsets [G + 1]; local_offsets [n_local + 1] (n_local = experts this rank owns):
+ *   the grouped order lists local expert 0's rows from every source (source order), then local
+ *   expert 1's, ...; recv_perm [max_rows]: grouped row -> receive row; recv_inv [max_rows]:
+ *   receive row -> grouped row.  Run the expert FFN on the received rows with
+ *   moe_expert_ffn(desc with T = rows, k = 1, N = n_local; x = receive buffer, perm = recv_perm,
+ *   offsets = local_offsets; the rank's own weight stacks).
+ *   max_rows: capacity of recv_perm / recv_inv; if the sources sent more rows
+ *   (recv_offsets[G] > max_rows) the entries past max_rows are not written.
+ *   Needs G * n_local <= 4096. */
+moe_status moe_ep_receive_layout(int32_t N, int32_t G, const int32_t *owner, int32_t rank,
+                                 const int32_t *recv_counts, int32_t max_rows, int32_t *recv_offsets,
+                                 int32_t *local_offsets, int32_t *recv_perm, int32_t *recv_inv,
+                                 moe_stream_t stream);
+
+/* After the expert FFN on a rank: ret[r] = y_grouped[recv_inv[r]] for every receive row r <
+ * min(recv_offsets[G], max_rows), i.e. the expert outputs in receive order, which the return
+ * exchange carries back (source s gets rows recv_offsets[s] .. recv_offsets[s+1]-1).  Each
+ * source then concatenates what it gets back in rank order, which is its send order, and runs
+ * moe_combine with its own inv and gate weights.
+ *   y_grouped and ret: max_rows rows each.  row_bytes: bytes per row (d * 4 for fp32 expert
+ *   outputs), a multiple of 16. */
+moe_status moe_ep_unpack(int32_t G, int32_t max_rows, int32_t row_bytes, const int32_t *recv_offsets,
+                         const int32_t *recv_inv, const void *y_grouped, void *ret, moe_stream_t stream);
+
 /* Static text of a status code. */
 const char *moe_status_str(moe_status s);
 /* Detail of the last error on the calling thread ("" if none). */

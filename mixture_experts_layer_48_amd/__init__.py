@@ -22,6 +22,7 @@ MOE_FFN_RELU2, MOE_FFN_SWIGLU = 0, 1
 MOE_NUM_STAGES = 6
 STAGE_NAMES = ("route", "capacity", "permute", "ffn_in", "ffn_out", "combine")
 MOE_NUM_STATS = 8
+MOE_EP_MAX_RANKS = 64
 STAT_NAMES = ("entropy_bits", "entropy_ideal_bits", "top3_share", "max_share", "cv", "balance_loss",
               "reroute_rate", "experts_touched")
 
@@ -84,8 +85,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_layer_forward_timed.argtypes = [pdesc, ctypes.POINTER(moe_weights), vp, vp,
                                             ctypes.POINTER(moe_routing), vp, sz, vp, ctypes.POINTER(vp)]
     lib.moe_routing_stats.argtypes = [pdesc, vp, vp, vp, ctypes.c_double, vp, vp, vp, vp, sz, vp]
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.moe_ep_dispatch.argtypes = [pdesc, vp, pi32, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_ep_receive_layout.argtypes = [ctypes.c_int32, ctypes.c_int32, pi32, ctypes.c_int32, vp,
+                                          ctypes.c_int32, vp, vp, vp, vp, vp]
+    lib.moe_ep_unpack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-              "moe_layer_forward_timed", "moe_routing_stats"):
+              "moe_layer_forward_timed", "moe_routing_stats", "moe_ep_dispatch", "moe_ep_receive_layout",
+              "moe_ep_unpack"):
         getattr(lib, f).restype = i32
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -183,6 +190,32 @@ def moe_routing_stats(desc, logits, idx, counts, stats, top3, ws, alpha: float =
                                             float(alpha), _ptr(stats), _ptr(top3), _ptr(prob_mean), _ptr(ws),
                                             0 if ws is None else ws.numel() * ws.element_size(),
                                             _stream(stream)), "moe_routing_stats")
+
+
+def _owner_arr(owner: Sequence[int]):
+    return (ctypes.c_int32 * len(owner))(*[int(v) for v in owner])
+
+
+def moe_ep_dispatch(desc, idx, owner: Sequence[int], G: int, counts, expert_offsets, send_counts, send_offsets,
+                    perm, inv, x=None, send_buf=None, stream=None) -> None:
+    """owner: host sequence [N] of ranks; the other tensors on the device."""
+    _check(load_library().moe_ep_dispatch(ctypes.byref(desc), _ptr(idx), _owner_arr(owner), int(G), _ptr(counts),
+                                          _ptr(expert_offsets), _ptr(send_counts), _ptr(send_offsets), _ptr(perm),
+                                          _ptr(inv), _ptr(x), _ptr(send_buf), _stream(stream)), "moe_ep_dispatch")
+
+
+def moe_ep_receive_layout(N: int, G: int, owner: Sequence[int], rank: int, recv_counts, max_rows: int,
+                          recv_offsets, local_offsets, recv_perm, recv_inv, stream=None) -> None:
+    _check(load_library().moe_ep_receive_layout(int(N), int(G), _owner_arr(owner), int(rank), _ptr(recv_counts),
+                                                int(max_rows), _ptr(recv_offsets), _ptr(local_offsets),
+                                                _ptr(recv_perm), _ptr(recv_inv), _stream(stream)),
+           "moe_ep_receive_layout")
+
+
+def moe_ep_unpack(G: int, max_rows: int, row_bytes: int, recv_offsets, recv_inv, y_grouped, ret,
+                  stream=None) -> None:
+    _check(load_library().moe_ep_unpack(int(G), int(max_rows), int(row_bytes), _ptr(recv_offsets), _ptr(recv_inv),
+                                        _ptr(y_grouped), _ptr(ret), _stream(stream)), "moe_ep_unpack")
 
 
 # ---------------------------------------------------------------- convenience

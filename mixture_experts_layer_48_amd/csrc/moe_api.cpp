@@ -314,6 +314,75 @@ moe_status moe_routing_stats(const moe_layer_desc* desc, const float* logits, co
     return e == hipSuccess ? MOE_OK : hip_fail(e, "routing statistics launch");
 }
 
+namespace {
+moe_status check_owner(const int32_t* owner, int N, int G) {
+    if (G < 1 || G > MOE_EP_MAX_RANKS) return fail(MOE_ERR_INVALID_ARG, "G must satisfy 1 <= G <= 64");
+    if (!owner) return fail(MOE_ERR_INVALID_ARG, "owner is NULL");
+    for (int e = 0; e < N; ++e)
+        if (owner[e] < 0 || owner[e] >= G)
+            return fail(MOE_ERR_INVALID_ARG, "owner[" + std::to_string(e) + "] outside [0, G)");
+    return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_ep_dispatch(const moe_layer_desc* desc, const int32_t* idx, const int32_t* owner, int32_t G,
+                           int32_t* counts, int32_t* expert_offsets, int32_t* send_counts, int32_t* send_offsets,
+                           int32_t* perm, int32_t* inv, const void* x, void* send_buf, moe_stream_t stream) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const moe_layer_desc& d = *desc;
+    if ((st = check_owner(owner, d.N, G)) != MOE_OK) return st;
+    if (d.T == 0) return MOE_OK;
+    if (!idx || !counts || !expert_offsets || !send_counts || !send_offsets || !perm || !inv)
+        return fail(MOE_ERR_INVALID_ARG, "idx, counts, expert_offsets, send_counts, send_offsets, perm and inv are required");
+    if ((x == nullptr) != (send_buf == nullptr)) return fail(MOE_ERR_INVALID_ARG, "give both x and send_buf or neither");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_ep_dispatch(idx, d.T, d.k, d.N, owner, G, counts, expert_offsets, send_counts,
+                                      send_offsets, perm, inv, s);
+    if (e != hipSuccess) return hip_fail(e, "ep dispatch launch");
+    if (send_buf) {
+        // rows of every destination, in send order: send row r <- x[perm[r] / k], r < send_offsets[G]
+        e = launch_gather_rows(x, perm, send_offsets, d.T, d.k, G, (int)(d.d * elem_bytes(d)), send_buf, s);
+        if (e != hipSuccess) return hip_fail(e, "ep pack launch");
+    }
+    return MOE_OK;
+}
+
+moe_status moe_ep_receive_layout(int32_t N, int32_t G, const int32_t* owner, int32_t rank,
+                                 const int32_t* recv_counts, int32_t max_rows, int32_t* recv_offsets,
+                                 int32_t* local_offsets, int32_t* recv_perm, int32_t* recv_inv,
+                                 moe_stream_t stream) {
+    g_err.clear();
+    if (N < 1 || N > 256) return fail(MOE_ERR_INVALID_ARG, "N must satisfy 1 <= N <= 256");
+    moe_status st = check_owner(owner, N, G);
+    if (st != MOE_OK) return st;
+    if (rank < 0 || rank >= G) return fail(MOE_ERR_INVALID_ARG, "rank outside [0, G)");
+    if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "max_rows < 0");
+    if (!recv_counts || !recv_offsets || !local_offsets || (max_rows > 0 && (!recv_perm || !recv_inv)))
+        return fail(MOE_ERR_INVALID_ARG, "recv_counts, recv_offsets, local_offsets, recv_perm and recv_inv are required");
+    int n_local = 0;
+    for (int e = 0; e < N; ++e) n_local += owner[e] == rank;
+    if ((long long)G * n_local > 4096) return fail(MOE_ERR_UNSUPPORTED, "G * n_local > 4096");
+    hipError_t e = launch_ep_receive_layout(recv_counts, N, G, owner, rank, max_rows, recv_offsets, local_offsets,
+                                            recv_perm, recv_inv, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "ep receive layout launch");
+}
+
+moe_status moe_ep_unpack(int32_t G, int32_t max_rows, int32_t row_bytes, const int32_t* recv_offsets,
+                         const int32_t* recv_inv, const void* y_grouped, void* ret, moe_stream_t stream) {
+    g_err.clear();
+    if (G < 1 || G > MOE_EP_MAX_RANKS) return fail(MOE_ERR_INVALID_ARG, "G must satisfy 1 <= G <= 64");
+    if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "max_rows < 0");
+    if (row_bytes < 16 || row_bytes % 16 != 0) return fail(MOE_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 16");
+    if (max_rows == 0) return MOE_OK;
+    if (!recv_offsets || !recv_inv || !y_grouped || !ret)
+        return fail(MOE_ERR_INVALID_ARG, "recv_offsets, recv_inv, y_grouped and ret are required");
+    hipError_t e = launch_ep_unpack(y_grouped, recv_inv, recv_offsets, G, max_rows, row_bytes, ret,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "ep unpack launch");
+}
+
 const char* moe_status_str(moe_status s) {
     switch (s) {
         case MOE_OK: return "MOE_OK";

@@ -10,6 +10,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define MOE_MAX_EXPERTS 256
+#define MOE_EP_MAX_RANKS 64     // expert-parallel ranks of the dispatch / receive layouts
+#define MOE_EP_MAX_BLOCKS 4096  // (source rank, local expert) pairs of one receive layout
 #define WAVE 64
 
 // Order-preserving map of an fp32 logit to uint32 (larger float -> larger key).

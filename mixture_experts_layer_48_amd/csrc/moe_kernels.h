@@ -49,3 +49,15 @@ size_t stats_workspace_bytes(int T, int N);
 hipError_t launch_routing_stats(const float* z, const int32_t* idx, const int32_t* counts, int T, int N, int k,
                                 double alpha, void* ws, double* stats, int32_t* top3, double* prob_mean,
                                 hipStream_t s);
+
+// Expert parallelism: send layout keyed by (owner rank, expert) (owner: host array [N], values in
+// [0, G)); receive layout over the sources' count vectors; unpack of the grouped expert outputs
+// into receive order.
+hipError_t launch_ep_dispatch(const int32_t* idx, int T, int k, int N, const int32_t* owner, int G,
+                              int32_t* counts, int32_t* expert_offsets, int32_t* send_counts,
+                              int32_t* send_offsets, int32_t* perm, int32_t* inv, hipStream_t s);
+hipError_t launch_ep_receive_layout(const int32_t* recv_counts, int N, int G, const int32_t* owner, int rank,
+                                    int max_rows, int32_t* recv_offsets, int32_t* local_offsets,
+                                    int32_t* recv_perm, int32_t* recv_inv, hipStream_t s);
+hipError_t launch_ep_unpack(const void* y_grouped, const int32_t* recv_inv, const int32_t* recv_offsets, int G,
+                            int max_rows, int row_bytes, void* ret, hipStream_t s);

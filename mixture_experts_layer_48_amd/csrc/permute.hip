@@ -2,6 +2,11 @@
 // sees one contiguous block of rows (page "MoE稀疏激活原理与工程实践：揭秘大模型参数幻觉",
 // section 3.1: tokens routed one by one, then regrouped by expert id before the experts run).
 //
+// The same kernel, keyed by (owner rank, expert), gives the expert-parallel send layout: each
+// destination rank's rows are one contiguous range (page "MoE 分片：混合專家模型的平行化策略",
+// sections 專家平行化詳解 and 動態 token 路由, steps 3-5: tokens go to the GPUs that own their
+// experts and come back for the combine).
+//
 // One block of 1024 threads does the whole grouping, deterministically and without atomics on
 // the output order:
 //   1. each wave counts its contiguous range of slots per expert (LDS histogram per wave);
@@ -16,11 +21,28 @@
 #define PM_THREADS 1024
 #define PM_WAVES (PM_THREADS / 64)
 
+// Destination-major keys for the expert-parallel send layout: experts are ordered by (owner
+// rank, expert id); pos[e] is expert e's place in that order, exp_at inverts it, and rank r's
+// experts occupy places rank_first[r] .. rank_first[r+1]-1.  Built on the host, passed by value.
+struct EpMapArg {
+    int pos[MOE_MAX_EXPERTS];
+    int exp_at[MOE_MAX_EXPERTS];
+    int rank_first[MOE_EP_MAX_RANKS + 1];
+    int G;
+};
+struct NoMapArg {};
+
+// EP = false: plain grouping by expert.  EP = true: grouping by (owner rank, expert), plus the
+// per-rank row counts and offsets.  In both, rows of one expert are in ascending slot order;
+// slots whose index is outside [0, N) are dropped (inv -1).
+template <bool EP, typename MapT>
 __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
     const int32_t* __restrict__ idx, int S, int N, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv, const MapT map,
+    int32_t* __restrict__ send_counts, int32_t* __restrict__ send_offsets) {
     __shared__ int hist[PM_WAVES][MOE_MAX_EXPERTS];
     __shared__ int offs[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_pos[MOE_MAX_EXPERTS];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     // equal contiguous ranges per wave, a multiple of 64 slots each
     const int per_wave = ((S + PM_WAVES * 64 - 1) / (PM_WAVES * 64)) * 64;
@@ -28,13 +50,22 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
     const int end = min(S, beg + per_wave);
 
     for (int i = tid; i < PM_WAVES * MOE_MAX_EXPERTS; i += PM_THREADS) (&hist[0][0])[i] = 0;
+    if constexpr (EP) {
+        for (int e = tid; e < N; e += PM_THREADS) s_pos[e] = map.pos[e];
+    }
     __syncthreads();
+    // key of a slot: its expert's place in the layout, or -1 (dropped)
+    auto key_of = [&](int e) -> int {
+        if (e < 0 || e >= N) return -1;
+        if constexpr (EP) return s_pos[e];
+        return e;
+    };
     for (int s = beg + lane; s < end; s += 64) {
-        const int e = idx[s];
+        const int e = key_of(idx[s]);
         if (e >= 0) atomicAdd(&hist[wave][e], 1);  // integer counts: order-independent
     }
     __syncthreads();
-    if (tid < 64) {  // one wave: totals, exclusive scan over experts
+    if (tid < 64) {  // one wave: totals, exclusive scan over places
         int tot[4], run = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -58,8 +89,10 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
             const int e = tid * 4 + q;
             if (e < N) {
                 offs[e] = base;
-                counts[e] = tot[q];
-                offsets[e] = base;
+                int ge = e;  // the expert at this place
+                if constexpr (EP) ge = map.exp_at[e];
+                counts[ge] = tot[q];
+                offsets[ge] = base;
             }
             base += tot[q];
         }
@@ -69,7 +102,13 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
         }
     }
     __syncthreads();
-    // per-wave starting row of each expert: offsets[e] + counts of e in earlier waves
+    if constexpr (EP) {
+        for (int r = tid; r <= map.G; r += PM_THREADS) {
+            send_offsets[r] = offs[map.rank_first[r]];
+            if (r < map.G) send_counts[r] = offs[map.rank_first[r + 1]] - offs[map.rank_first[r]];
+        }
+    }
+    // per-wave starting row of each place: offs[e] + counts of e in earlier waves
     for (int e = tid; e < N; e += PM_THREADS) {
         int run = offs[e];
         for (int ww = 0; ww < PM_WAVES; ++ww) {
@@ -82,7 +121,7 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
     for (int g = 0; g < per_wave; g += 64) {
         const int s = beg + g + lane;
         const bool valid = s < end;
-        const int e = valid ? idx[s] : -1;
+        const int e = valid ? key_of(idx[s]) : -1;
         const uint64_t eq = match_lanes<9>((uint32_t)(e + 1));
         const uint64_t lt = lanemask_lt();
         if (e >= 0) {
@@ -120,8 +159,30 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
 hipError_t launch_permute(const int32_t* idx, int T, int k, int N, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, hipStream_t s) {
     const int S = T * k;
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PM_THREADS), 0, s, idx, S, N, counts, offsets,
-                       perm, inv);
+    permute_kernel<false, NoMapArg><<<1, PM_THREADS, 0, s>>>(idx, S, N, counts, offsets, perm, inv, NoMapArg{},
+                                                             nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_ep_dispatch(const int32_t* idx, int T, int k, int N, const int32_t* owner, int G,
+                              int32_t* counts, int32_t* expert_offsets, int32_t* send_counts,
+                              int32_t* send_offsets, int32_t* perm, int32_t* inv, hipStream_t s) {
+    // places ordered by (owner, expert id): a counting sort over the ranks
+    EpMapArg m{};
+    m.G = G;
+    int nper[MOE_EP_MAX_RANKS] = {0};
+    for (int e = 0; e < N; ++e) nper[owner[e]]++;
+    m.rank_first[0] = 0;
+    for (int r = 0; r < G; ++r) m.rank_first[r + 1] = m.rank_first[r] + nper[r];
+    int next[MOE_EP_MAX_RANKS];
+    for (int r = 0; r < G; ++r) next[r] = m.rank_first[r];
+    for (int e = 0; e < N; ++e) {
+        const int p = next[owner[e]]++;
+        m.pos[e] = p;
+        m.exp_at[p] = e;
+    }
+    permute_kernel<true, EpMapArg><<<1, PM_THREADS, 0, s>>>(idx, T * k, N, counts, expert_offsets, perm, inv, m,
+                                                           send_counts, send_offsets);
     return hipGetLastError();
 }
 

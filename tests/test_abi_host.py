@@ -143,10 +143,38 @@ def test_routing_stats_argument_errors(lib):
     assert b"workspace" in lib.moe_last_error() or b"k must" in lib.moe_last_error()
 
 
+def test_ep_argument_errors(lib):
+    desc = _desc(T=100, N=8, k=2)
+    own = lambda v: (ctypes.c_int32 * len(v))(*v)  # noqa: E731
+    ok = own([0, 0, 1, 1, 2, 2, 3, 3])
+    F = [FAKE] * 6
+    # owner out of range, G out of range, missing outputs, x without send_buf
+    assert lib.moe_ep_dispatch(ctypes.byref(desc), FAKE, own([0, 0, 1, 1, 2, 2, 3, 4]), 4, *F, None, None,
+                               None) == M.MOE_ERR_INVALID_ARG
+    assert b"owner[7]" in lib.moe_last_error()
+    assert lib.moe_ep_dispatch(ctypes.byref(desc), FAKE, ok, 0, *F, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_ep_dispatch(ctypes.byref(desc), FAKE, ok, 65, *F, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_ep_dispatch(ctypes.byref(desc), FAKE, None, 4, *F, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_ep_dispatch(ctypes.byref(desc), FAKE, ok, 4, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None,
+                               None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_ep_dispatch(ctypes.byref(desc), FAKE, ok, 4, *F, FAKE, None, None) == M.MOE_ERR_INVALID_ARG
+    # receive layout: rank outside [0, G), too many (source, local expert) pairs, missing outputs
+    assert lib.moe_ep_receive_layout(8, 4, ok, 4, FAKE, 10, FAKE, FAKE, FAKE, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    big = own([0] * 256)
+    assert lib.moe_ep_receive_layout(256, 64, big, 0, FAKE, 10, FAKE, FAKE, FAKE, FAKE, None) \
+        == M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_ep_receive_layout(8, 4, ok, 1, FAKE, 10, FAKE, None, FAKE, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    # unpack: row size not a multiple of 16, missing buffers
+    assert lib.moe_ep_unpack(4, 10, 24, FAKE, FAKE, FAKE, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_ep_unpack(4, 10, 32, FAKE, None, FAKE, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_ep_unpack(4, 0, 32, None, None, None, None, None) == M.MOE_OK
+
+
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define MOE_NUM_STATS (\d+)", text).group(1)) == M.MOE_NUM_STATS == len(M.STAT_NAMES)
     assert int(re.search(r"#define MOE_NUM_STAGES (\d+)", text).group(1)) == M.MOE_NUM_STAGES
+    assert int(re.search(r"#define MOE_EP_MAX_RANKS (\d+)", text).group(1)) == M.MOE_EP_MAX_RANKS
     block = text[text.index("#define MOE_NUM_STATS") - 1200:text.index("#define MOE_NUM_STATS")]
     listed = re.findall(r"\*\s+\d\s+([a-z0-9_]+)", block)
     assert tuple(listed) == M.STAT_NAMES

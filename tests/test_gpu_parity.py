@@ -95,6 +95,7 @@ SMALL = {
     "switch_small": C["switch_top1"].replace(name="switch_small", T=3000, d=128, d_ff=256),
     "scout_small": C["scout_top1"].replace(name="scout_small", T=600, d=256, d_ff=384),
     "v4_small": C["v4_shared_top7"].replace(name="v4_small", T=260, d=128, d_ff=192),
+    "maverick_small": C["maverick_top1"].replace(name="maverick_small", T=2000, d=128, d_ff=192),
 }
 
 
@@ -200,9 +201,9 @@ def test_stage_entry_points_compose_to_forward():
 
 
 FULL = ["mixtral_prefill", "mixtral_decode", "deepseek_v3", "skewed_capacity", "switch_top1", "scout_top1",
-        "v4_shared_top7"]
+        "v4_shared_top7", "maverick_top1"]
 SAMPLE_TOKENS = {"mixtral_prefill": 8, "mixtral_decode": 16, "deepseek_v3": 4, "skewed_capacity": 8,
-                 "switch_top1": 8, "scout_top1": 8, "v4_shared_top7": 4}
+                 "switch_top1": 8, "scout_top1": 8, "v4_shared_top7": 4, "maverick_top1": 6}
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -50,7 +50,7 @@ import torch
 # tensor streams (one generator stream per tensor)
 STREAM_X, STREAM_ROUTER, STREAM_GATE, STREAM_UP, STREAM_DOWN = 1, 2, 3, 4, 5
 STREAM_SH_GATE, STREAM_SH_UP, STREAM_SH_DOWN = 6, 7, 8
-STREAM_GRID, STREAM_GRID_BIAS, STREAM_LOGITS = 9, 10, 11
+STREAM_GRID, STREAM_GRID_BIAS, STREAM_LOGITS, STREAM_TOKENS, STREAM_OWNER = 9, 10, 11, 12, 13
 
 FFN_RELU2 = "relu2"
 FFN_SWIGLU = "swiglu"
@@ -108,8 +108,9 @@ CONFIGS: Dict[str, LayerConfig] = {
                                    capacity_factor=2.0, zipf_bias=True, seed=1005),
     # Routing variants the pages name without layer widths (those are taken from the layers
     # above): top-1 over 128 experts with two-layer ReLU experts (Switch-style), top-1 over 16
-    # SwiGLU experts (Llama 4 Scout-style), and one shared expert plus top-7 of 256 routed ones
-    # (the DeepSeek-V4 description: 8 active experts, the shared one included).
+    # SwiGLU experts (Llama 4 Scout-style), one shared expert plus top-7 of 256 routed ones
+    # (the DeepSeek-V4 description: 8 active experts, the shared one included), and top-1
+    # over 128 SwiGLU experts.
     "switch_top1": LayerConfig("switch_top1", T=4096, d=4096, N=128, k=1, d_ff=14336,
                                dtype="bf16", ffn=FFN_RELU2, gating=GATE_TOPK_SOFTMAX, seed=1006),
     "scout_top1": LayerConfig("scout_top1", T=4096, d=4096, N=16, k=1, d_ff=14336,
@@ -117,6 +118,11 @@ CONFIGS: Dict[str, LayerConfig] = {
     "v4_shared_top7": LayerConfig("v4_shared_top7", T=8192, d=7168, N=256, k=7, d_ff=2048,
                                   dtype="bf16", ffn=FFN_SWIGLU, gating=GATE_SOFTMAX_TOPK,
                                   has_shared=True, seed=1008),
+    # 128 experts with the 16-expert layer's active size per token (Llama 4 Maverick-style: the
+    # page gives 128 experts per layer and the same active parameters as the top-1 16-expert
+    # layer, read here as top-1 over 128 SwiGLU experts of the same width)
+    "maverick_top1": LayerConfig("maverick_top1", T=4096, d=4096, N=128, k=1, d_ff=14336,
+                                 dtype="bf16", ffn=FFN_SWIGLU, gating=GATE_TOPK_SOFTMAX, seed=1009),
 }
 
 
@@ -206,6 +212,32 @@ def make_logits(T: int, N: int, seed: int, device="cpu", levels: Optional[int] =
     if levels is None:
         return torch.randn((T, N), generator=g, device=device, dtype=torch.float32)
     return torch.randint(-(levels // 2), levels - levels // 2, (T, N), generator=g, device=device).float() / 8.0
+
+
+def make_tokens(T: int, d: int, dtype: str, seed: int, device="cpu", grid_cols: int = 0,
+                levels: int = 16) -> torch.Tensor:
+    """One rank's tokens x [T, d] ~ N(0, 1) in `dtype`; with grid_cols, columns :grid_cols take
+    values k/8 for integer k uniform in [-levels/2, levels/2) (for a selection router)."""
+    device = torch.device(device)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = _normal((T, d), 1.0, dt, device, _gen(device, seed, STREAM_TOKENS))
+    if grid_cols:
+        g = _gen(device, seed, STREAM_GRID)
+        steps = torch.randint(-(levels // 2), levels - levels // 2, (T, grid_cols), generator=g, device=device)
+        x[:, :grid_cols] = (steps.float() / 8.0).to(dt)
+    return x
+
+
+def make_owner_map(N: int, G: int, kind: str = "contiguous", seed: int = 0):
+    """Expert -> rank map of an expert-parallel placement: "contiguous" (rank r owns a block of
+    about N/G experts), "interleaved" (expert e on rank e % G) or "random" (uniform ranks,
+    seeded; a rank may own none)."""
+    if kind == "contiguous":
+        return [e * G // N for e in range(N)]
+    if kind == "interleaved":
+        return [e % G for e in range(N)]
+    g = _gen(torch.device("cpu"), seed, STREAM_OWNER)
+    return [int(v) for v in torch.randint(0, G, (N,), generator=g)]
 
 
 def scaled(cfg: LayerConfig, **kw) -> LayerConfig:
