@@ -25,7 +25,8 @@ The layer (one GPU's whole expert set, no cross-device step):
   6. shared expert on every token (optional)        [P4 专家粒度; P3 DeepSeek-V4 架构细节]
   7. gate-weighted combine                          [P1 動態 token 路由 step 6; P2 代码]
 Beside the layer: routing statistics [P5 §4.2, §2.2/§3.3; P3 核心机制] and the
-send / receive layouts of expert parallelism [P1 專家平行化詳解, 動態 token 路由].
+send / receive layouts of expert parallelism [P1 專家平行化詳解, 動態 token 路由];
+int4 expert weights (a format defined here: the pages name INT4 experts only).
 
 Readings taken where the pages leave a step open (each also listed in the
 design notes): equal logits rank the lower expert id first; slot 0 is the
@@ -59,6 +60,7 @@ __all__ = [
     "capacity_route", "route_from_logits", "group_by_expert", "silu", "expert_ffn",
     "combine", "forward", "param_counts", "near_tie_tokens", "routing_stats",
     "ep_dispatch_layout", "ep_receive_layout",
+    "Q4_GROUP", "quantize_q4", "dequantize_q4", "pack_q4", "unpack_q4",
 ]
 
 
@@ -360,6 +362,86 @@ def ep_receive_layout(recv_counts, owner: Sequence[int], rank: int) -> Dict[str,
         local_offsets[le + 1] = local_offsets[le] + int(rc[:, e].sum())
     return dict(recv_offsets=recv_offsets, local_offsets=local_offsets, recv_perm=recv_perm,
                 recv_inv=recv_inv, local_experts=np.array(local, dtype=np.int64))
+
+
+# ---------------------------------------------------------------- int4 expert weights
+Q4_GROUP = 128      # input features per scale group
+
+
+def quantize_q4(w):
+    """Weight-only int4 quantisation of one weight matrix [rows, K] (the
+    pages name GPTQ/AWQ INT4 expert weights at a quarter of the memory, [P3]
+    DeepSeek-V4的MoE架构工程细节 and [P5] §3.1's AWQ deployment, and give no
+    format; this one is defined here).
+
+    Per row and group of Q4_GROUP consecutive inputs: scale = amax / 7 with
+    amax the largest |w| of the group, and q = clamp(rint(w / scale), -8, 7)
+    (round half to even); an all-zero group has scale 0 and q = 0.  The
+    scale and the division are taken in fp32, the precision in which the
+    kernel decides the codes.  Returns q [rows, K] int8 and scales
+    [rows, K / Q4_GROUP] fp32.  The weight it stands for is scale * q.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    rows, K = w.shape
+    G = K // Q4_GROUP
+    q = np.zeros((rows, K), dtype=np.int8)
+    scales = np.zeros((rows, G), dtype=np.float32)
+    for r in range(rows):
+        for g in range(G):
+            blk = w[r, g * Q4_GROUP:(g + 1) * Q4_GROUP]
+            amax = np.float32(np.max(np.abs(blk)))
+            if amax == 0:
+                continue
+            sc = np.float32(amax / np.float32(7.0))
+            scales[r, g] = sc
+            q[r, g * Q4_GROUP:(g + 1) * Q4_GROUP] = np.clip(np.rint(blk / sc), -8, 7).astype(np.int8)
+    return q, scales
+
+
+def dequantize_q4(q, scales):
+    """The weight an int4 matrix stands for: scale[r, g] * q[r, k] for k in
+    group g, exactly (float64)."""
+    q = np.asarray(q, dtype=np.float64)
+    sc = np.repeat(np.asarray(scales, dtype=np.float64), Q4_GROUP, axis=1)
+    return sc * q
+
+
+def pack_q4(q):
+    """Codes (q + 8, four bits each) of a [rows, K] int4 matrix as uint32
+    words [rows, K / 8].  Words follow the order the kernel loads them in:
+    within row r and group g, word a*4 + s (a, s in 0..3) holds the inputs
+    k = 128 g + 32 s + 8 a + i, i = 0..7, with input i's code at bit
+    4 * (i // 2) + 16 * (i % 2).
+    """
+    q = np.asarray(q, dtype=np.int64)
+    rows, K = q.shape
+    words = np.zeros((rows, K // 8), dtype=np.uint32)
+    for r in range(rows):
+        for g in range(K // Q4_GROUP):
+            for a in range(4):
+                for s_ in range(4):
+                    v = 0
+                    for i in range(8):
+                        k = Q4_GROUP * g + 32 * s_ + 8 * a + i
+                        v |= (int(q[r, k]) + 8) << (4 * (i // 2) + 16 * (i % 2))
+                    words[r, 16 * g + 4 * a + s_] = v
+    return words
+
+
+def unpack_q4(words, K: int):
+    """Inverse of pack_q4: q [rows, K] from the words."""
+    words = np.asarray(words, dtype=np.int64)
+    rows = words.shape[0]
+    q = np.zeros((rows, K), dtype=np.int8)
+    for r in range(rows):
+        for g in range(K // Q4_GROUP):
+            for a in range(4):
+                for s_ in range(4):
+                    v = int(words[r, 16 * g + 4 * a + s_])
+                    for i in range(8):
+                        k = Q4_GROUP * g + 32 * s_ + 8 * a + i
+                        q[r, k] = ((v >> (4 * (i // 2) + 16 * (i % 2))) & 0xF) - 8
+    return q
 
 
 # ---------------------------------------------------------------- counting

@@ -556,3 +556,58 @@ def test_ep_round_trip_brute_force():
                 assert returned[disp[s]["inv"][slot]] == (s, slot)
             else:
                 assert disp[s]["inv"][slot] == -1
+
+
+# ---------------------------------------------------------------- int4 expert weights
+def test_q4_pack_hand_worked_word():
+    # one row, one group: q = k mod 16 - 8 for k < 128.  Word a*4 + s holds k = 32 s + 8 a + i with
+    # code (k mod 16) at bit 4 (i // 2) + 16 (i % 2).  Word 0 (a = 0, s = 0): k = 0..7, codes 0..7:
+    # low half nibbles 0, 2, 4, 6 -> 0x6420, high half 1, 3, 5, 7 -> 0x7531.
+    q = np.array([[(k % 16) - 8 for k in range(128)]])
+    w = O.pack_q4(q)
+    assert int(w[0, 0]) == 0x75316420
+    # word 4 (a = 1, s = 0): k = 8..15, codes 8..15 -> low 8, 10, 12, 14 and high 9, 11, 13, 15
+    assert int(w[0, 4]) == 0xFDB9ECA8
+    # word 1 (a = 0, s = 1): k = 32..39, codes 0..7 again
+    assert int(w[0, 1]) == 0x75316420
+    assert np.array_equal(O.unpack_q4(w, 128), q)
+
+
+def test_q4_pack_round_trip_random():
+    rng = np.random.default_rng(31)
+    q = rng.integers(-8, 8, size=(5, 384))
+    assert np.array_equal(O.unpack_q4(O.pack_q4(q), 384), q)
+
+
+def test_q4_quantize_bounds_and_grid():
+    rng = np.random.default_rng(32)
+    w = (rng.standard_normal((6, 256)) * 0.02).astype(np.float32)
+    w[2, 128:] = 0.0                                   # an all-zero group
+    q, sc = O.quantize_q4(w)
+    assert q.min() >= -7 and q.max() <= 7            # scale = amax / 7: the codes stay symmetric
+    assert sc[2, 1] == 0 and np.all(q[2, 128:] == 0)
+    wh = O.dequantize_q4(q, sc)
+    # round to nearest: each weight is within half a step of its code's value
+    step = np.repeat(sc.astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(wh - w) <= 0.5 * step * (1 + 1e-6) + 1e-12)
+    # the largest |w| of every nonzero group maps to +-7
+    for r in range(6):
+        for g in range(2):
+            blk = np.abs(w[r, 128 * g:128 * (g + 1)])
+            if blk.max() > 0:
+                assert abs(int(q[r, 128 * g + int(np.argmax(blk))])) == 7
+    # weights already on a group's grid come back exactly
+    grid = (np.arange(-7, 8, dtype=np.float32) * np.float32(0.125))
+    wg = np.tile(grid, 20)[:256].reshape(1, 256).astype(np.float32)
+    wg[0, 0] = np.float32(0.875)                        # amax 7/8 in both groups -> scale 1/8
+    wg[0, 128] = np.float32(-0.875)
+    q2, sc2 = O.quantize_q4(wg)
+    assert np.all(sc2 == np.float32(0.125)) and np.array_equal(O.dequantize_q4(q2, sc2), wg.astype(np.float64))
+
+
+def test_q4_rounding_ties_to_even():
+    # amax 7 -> scale exactly 1; w = 2.5 and -0.5 are ties: rint gives 2 and -0 (to even)
+    w = np.zeros((1, 128), dtype=np.float32)
+    w[0, :4] = [7.0, 2.5, -0.5, 3.5]
+    q, sc = O.quantize_q4(w)
+    assert sc[0, 0] == 1.0 and q[0, :4].tolist() == [7, 2, 0, 4]
