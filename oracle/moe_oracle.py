@@ -383,19 +383,13 @@ def quantize_q4(w):
     """
     w = np.asarray(w, dtype=np.float32)
     rows, K = w.shape
-    G = K // Q4_GROUP
-    q = np.zeros((rows, K), dtype=np.int8)
-    scales = np.zeros((rows, G), dtype=np.float32)
-    for r in range(rows):
-        for g in range(G):
-            blk = w[r, g * Q4_GROUP:(g + 1) * Q4_GROUP]
-            amax = np.float32(np.max(np.abs(blk)))
-            if amax == 0:
-                continue
-            sc = np.float32(amax / np.float32(7.0))
-            scales[r, g] = sc
-            q[r, g * Q4_GROUP:(g + 1) * Q4_GROUP] = np.clip(np.rint(blk / sc), -8, 7).astype(np.int8)
-    return q, scales
+    blk = w.reshape(rows, K // Q4_GROUP, Q4_GROUP)
+    amax = np.max(np.abs(blk), axis=2)                              # [rows, groups], exact
+    scales = (amax / np.float32(7.0)).astype(np.float32)            # fp32 division
+    safe = np.where(scales > 0, scales, np.float32(1.0))[:, :, None]
+    q = np.clip(np.rint(blk / safe), -8, 7)                          # fp32 division, ties to even
+    q = np.where(amax[:, :, None] > 0, q, 0).astype(np.int8)         # all-zero group: q = 0
+    return q.reshape(rows, K), scales
 
 
 def dequantize_q4(q, scales):
