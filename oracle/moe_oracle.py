@@ -409,33 +409,21 @@ def pack_q4(q):
     """
     q = np.asarray(q, dtype=np.int64)
     rows, K = q.shape
-    words = np.zeros((rows, K // 8), dtype=np.uint32)
-    for r in range(rows):
-        for g in range(K // Q4_GROUP):
-            for a in range(4):
-                for s_ in range(4):
-                    v = 0
-                    for i in range(8):
-                        k = Q4_GROUP * g + 32 * s_ + 8 * a + i
-                        v |= (int(q[r, k]) + 8) << (4 * (i // 2) + 16 * (i % 2))
-                    words[r, 16 * g + 4 * a + s_] = v
-    return words
+    c = (q + 8).astype(np.uint64).reshape(rows, K // Q4_GROUP, 4, 4, 8)   # [r, g, s, a, i]
+    c = c.transpose(0, 1, 3, 2, 4)                                      # [r, g, a, s, i]
+    shift = np.array([4 * (i // 2) + 16 * (i % 2) for i in range(8)], dtype=np.uint64)
+    words = np.bitwise_or.reduce(c << shift, axis=4)                     # [r, g, a, s]
+    return words.reshape(rows, K // 8).astype(np.uint32)
 
 
 def unpack_q4(words, K: int):
     """Inverse of pack_q4: q [rows, K] from the words."""
     words = np.asarray(words, dtype=np.int64)
     rows = words.shape[0]
-    q = np.zeros((rows, K), dtype=np.int8)
-    for r in range(rows):
-        for g in range(K // Q4_GROUP):
-            for a in range(4):
-                for s_ in range(4):
-                    v = int(words[r, 16 * g + 4 * a + s_])
-                    for i in range(8):
-                        k = Q4_GROUP * g + 32 * s_ + 8 * a + i
-                        q[r, k] = ((v >> (4 * (i // 2) + 16 * (i % 2))) & 0xF) - 8
-    return q
+    w = words.reshape(rows, K // Q4_GROUP, 4, 4, 1)                       # [r, g, a, s, 1]
+    shift = np.array([4 * (i // 2) + 16 * (i % 2) for i in range(8)], dtype=np.int64)
+    q = ((w >> shift) & 0xF) - 8                                         # [r, g, a, s, i]
+    return q.transpose(0, 1, 3, 2, 4).reshape(rows, K).astype(np.int8)   # [r, g, s, a, i]
 
 
 # ---------------------------------------------------------------- counting
