@@ -69,7 +69,7 @@ class HipEvents:
         self.hip.hipEventDestroy(ev)
 
 
-def algorithmic_counts(cfg, counts):
+def algorithmic_counts(cfg, counts, weight_bytes: float = None):
     """Flops and bytes of one layer call by the definitions (not the implementation).
 
     flops: router 2*T*d*N; per kept (token, expert) slot 2*nm*d*d_ff (nm = 3 SwiGLU, 2 ReLU);
@@ -80,14 +80,15 @@ def algorithmic_counts(cfg, counts):
     nm = 3 if cfg.ffn == "swiglu" else 2
     nm_in = nm - 1
     eb = cfg.elem_bytes
+    wb = eb if weight_bytes is None else weight_bytes    # bytes per expert weight
     kept = int(np.sum(counts))
     touched = int(np.sum(counts > 0))
     rows_sh = cfg.T if cfg.has_shared else 0
     flops = 2.0 * cfg.T * cfg.d * cfg.N + 2.0 * nm * cfg.d * cfg.d_ff * (kept + rows_sh)
-    w_expert = nm * cfg.d * cfg.d_ff * eb
+    w_expert = nm * cfg.d * cfg.d_ff * wb
     bytes_ = (touched + (1 if cfg.has_shared else 0)) * w_expert + cfg.N * cfg.d * eb + 2 * cfg.T * cfg.d * eb
     ffn_in_flops = 2.0 * nm_in * cfg.d * cfg.d_ff * (kept + rows_sh)
-    ffn_in_bytes = ((touched + (1 if cfg.has_shared else 0)) * nm_in * cfg.d * cfg.d_ff * eb
+    ffn_in_bytes = ((touched + (1 if cfg.has_shared else 0)) * nm_in * cfg.d * cfg.d_ff * wb
                     + cfg.T * cfg.d * eb + (kept + rows_sh) * cfg.d_ff * eb)
     return dict(flops=flops, bytes=bytes_, touched=touched, kept=kept,
                 ffn_in_flops=ffn_in_flops, ffn_in_bytes=ffn_in_bytes)
@@ -274,6 +275,8 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default="mixtral_prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weights", choices=("native", "int4"), default="native",
+                    help="expert weights: the layer dtype, or int4 codes + fp32 group scales (0.53125 B each)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB", "COMMAND"),
@@ -309,7 +312,8 @@ def main(argv=None) -> int:
     inp = W.make_inputs(cfg, "cuda")
     desc = M.make_desc(cfg.T, cfg.d, cfg.N, cfg.k, cfg.d_ff, cfg.dtype, cfg.ffn, cfg.gating,
                        cfg.capacity_factor, cfg.has_shared)
-    layer = M.MoELayer(desc, inp)
+    qweights = M.quantize_weights_q4(inp) if args.weights == "int4" else None
+    layer = M.MoELayer(desc, inp, qweights=qweights)
     routing = layer.routing_buffers()
     y = torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device="cuda")
     hip = HipEvents()
@@ -364,7 +368,7 @@ def main(argv=None) -> int:
                      "top3": st_out["top3"].cpu().numpy().tolist()}
 
     counts = routing["counts"].cpu().numpy()
-    alg = algorithmic_counts(cfg, counts)
+    alg = algorithmic_counts(cfg, counts, weight_bytes=0.5 + 4.0 / 128 if qweights is not None else None)
     tokens_per_s = cfg.T * args.steps / (t1 - t0)
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     ai = alg["ffn_in_flops"] / alg["ffn_in_bytes"]
@@ -378,8 +382,9 @@ def main(argv=None) -> int:
         roof = {"bound": "hbm", "achieved": alg["ffn_in_bytes"] / (ffn_in_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_from_profile(cfg.name)
-    roof["kernel"] = "ffn_in (grouped gate/up projection)"
+    roof["traffic"] = traffic_from_profile(cfg.name) if qweights is None else None
+    roof["kernel"] = ("ffn_in (grouped gate/up projection)" if qweights is None
+                      else "ffn_in (gate/up projection, int4 weight stream)")
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -391,11 +396,11 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": cfg.dtype if qweights is None else "bf16 activations, int4 expert weights",
         "data": "synthetic (seeded Gaussian inputs and weights of the layer's shapes)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "N": cfg.N, "k": cfg.k, "d_ff": cfg.d_ff,
                    "ffn": cfg.ffn, "gating": cfg.gating, "capacity_factor": cfg.capacity_factor,
-                   "shared_expert": cfg.has_shared},
+                   "shared_expert": cfg.has_shared, "expert_weights": args.weights},
         "layer": {"tflops": alg["flops"] / (ms_per_step * 1e-3) / 1e12,
                   "mfma_frac": alg["flops"] / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "gbs_distinct_experts": alg["bytes"] / (ms_per_step * 1e-3) / 1e9,

@@ -223,6 +223,48 @@ moe_status moe_routing_stats(const moe_layer_desc *desc, const float *logits, co
                              const int32_t *counts, double alpha, double *stats, int32_t *top3,
                              double *prob_mean, void *ws, size_t ws_bytes, moe_stream_t stream);
 
+/* ---- Int4 expert weights for weight-streaming (decode) layers [P3 DeepSeek-V4的MoE架构工程细节:
+ * GPTQ/AWQ INT4 expert weights at a quarter of the memory; the pages give no format].  Format:
+ * per weight row and group of 128 consecutive inputs, scale = amax / 7 (fp32), q =
+ * clamp(rint(w / scale), -8, 7) (fp32 division, ties to even; all-zero group: scale 0, q 0); the
+ * weight stands for scale * q.  Codes q + 8, four bits each, eight per uint32: within row r and
+ * group g, word 4a + s (a, s in 0..3) holds inputs k = 128g + 32s + 8a + i (i = 0..7), input i
+ * at bit 4 (i / 2) + 16 (i % 2).  A stack of n matrices [rows, K]: codes [n, rows, K / 8] uint32,
+ * scales [n, K / 128, rows] fp32 (device). */
+typedef struct {
+    const uint32_t *codes;
+    const float *scales;
+} moe_q4_matrix;
+
+/* Layer weights with int4 experts; the router stays in the layer dtype (bf16). */
+typedef struct {
+    const void *w_router;      /* [N, d] bf16 */
+    const float *logit_bias;   /* [N] fp32, or NULL */
+    moe_q4_matrix w_gate;      /* [N, d_ff, d]; unused for MOE_FFN_RELU2 */
+    moe_q4_matrix w_up;        /* [N, d_ff, d] (W1 for RELU2) */
+    moe_q4_matrix w_down;      /* [N, d, d_ff] */
+    moe_q4_matrix sh_gate, sh_up, sh_down;   /* shared expert, as the routed ones */
+} moe_weights_q4;
+
+/* Quantise n_mats bf16 matrices w [n_mats, rows, K] (device) to the format above.
+ * K % 128 == 0 (MOE_ERR_UNSUPPORTED otherwise). */
+moe_status moe_quantize_q4(const void *w, int32_t n_mats, int32_t rows, int32_t K, uint32_t *codes,
+                           float *scales, moe_stream_t stream);
+
+/* moe_expert_ffn with int4 expert weights: every expert runs as a weight stream (one 16-row
+ * tile at a time, the decode regime; larger batches are correct but re-read the weights per
+ * tile).  Needs a bf16 layer with d % 128 == 0 and d_ff % 128 == 0.  Other arguments as
+ * moe_expert_ffn. */
+moe_status moe_expert_ffn_q4(const moe_layer_desc *desc, const moe_weights_q4 *weights,
+                             const void *x, const int32_t *perm, const int32_t *offsets,
+                             const float *row_scale, void *y_perm, void *ws, size_t ws_bytes,
+                             moe_stream_t stream);
+
+/* moe_layer_forward_timed with int4 expert weights (events may be NULL). */
+moe_status moe_layer_forward_q4(const moe_layer_desc *desc, const moe_weights_q4 *weights,
+                                const void *x, void *y, const moe_routing *routing, void *ws,
+                                size_t ws_bytes, moe_stream_t stream, void *const *events);
+
 /* ---- Expert parallelism: the layouts either side of the two all-to-alls [P1 專家平行化詳解 (each
  * GPU owns a subset of the experts; two all-to-alls per layer), P1 動態 token 路由 steps 3-6 (tokens
  * go to the GPUs owning their experts, the outputs come back, the combine runs at the origin)].

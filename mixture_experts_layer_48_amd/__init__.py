@@ -49,6 +49,15 @@ class moe_weights(ctypes.Structure):
                 ("w_router", "logit_bias", "w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")]
 
 
+class moe_q4_matrix(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class moe_weights_q4(ctypes.Structure):
+    _fields_ = [("w_router", ctypes.c_void_p), ("logit_bias", ctypes.c_void_p)] + \
+               [(n, moe_q4_matrix) for n in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")]
+
+
 class moe_routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("logits", "idx", "w", "counts", "offsets", "perm", "inv")]
 
@@ -86,13 +95,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.POINTER(moe_routing), vp, sz, vp, ctypes.POINTER(vp)]
     lib.moe_routing_stats.argtypes = [pdesc, vp, vp, vp, ctypes.c_double, vp, vp, vp, vp, sz, vp]
     pi32 = ctypes.POINTER(ctypes.c_int32)
+    pq4 = ctypes.POINTER(moe_weights_q4)
+    lib.moe_quantize_q4.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    lib.moe_expert_ffn_q4.argtypes = [pdesc, pq4, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_layer_forward_q4.argtypes = [pdesc, pq4, vp, vp, ctypes.POINTER(moe_routing), vp, sz, vp,
+                                         ctypes.POINTER(vp)]
     lib.moe_ep_dispatch.argtypes = [pdesc, vp, pi32, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_ep_receive_layout.argtypes = [ctypes.c_int32, ctypes.c_int32, pi32, ctypes.c_int32, vp,
                                           ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.moe_ep_unpack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
               "moe_layer_forward_timed", "moe_routing_stats", "moe_ep_dispatch", "moe_ep_receive_layout",
-              "moe_ep_unpack"):
+              "moe_ep_unpack", "moe_quantize_q4", "moe_expert_ffn_q4", "moe_layer_forward_q4"):
         getattr(lib, f).restype = i32
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -218,6 +232,61 @@ def moe_ep_unpack(G: int, max_rows: int, row_bytes: int, recv_offsets, recv_inv,
                                         _ptr(y_grouped), _ptr(ret), _stream(stream)), "moe_ep_unpack")
 
 
+def moe_quantize_q4(w, codes, scales, stream=None) -> None:
+    """w: bf16 device tensor [n_mats, rows, K] (or [rows, K]); codes uint32-sized [.., rows, K/8]
+    (int32 storage is fine); scales fp32 [n_mats, K/128, rows]."""
+    shape = tuple(w.shape)
+    n_mats, rows, K = (1,) + shape if len(shape) == 2 else shape
+    _check(load_library().moe_quantize_q4(_ptr(w), n_mats, rows, K, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_q4")
+
+
+def _weights_q4(q: Dict) -> moe_weights_q4:
+    def m(name):
+        return moe_q4_matrix(_ptr(q.get(name + "_codes")), _ptr(q.get(name + "_scales")))
+    return moe_weights_q4(_ptr(q.get("w_router")), _ptr(q.get("logit_bias")),
+                          *(m(n) for n in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")))
+
+
+def moe_expert_ffn_q4(desc, qweights: Dict, x, perm, offsets, row_scale, y_perm, ws, stream=None) -> None:
+    wt = _weights_q4(qweights)
+    _check(load_library().moe_expert_ffn_q4(ctypes.byref(desc), ctypes.byref(wt), _ptr(x), _ptr(perm),
+                                            _ptr(offsets), _ptr(row_scale), _ptr(y_perm), _ptr(ws),
+                                            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_expert_ffn_q4")
+
+
+def moe_layer_forward_q4(desc, qweights: Dict, x, y, routing: Optional[Dict] = None, ws=None, stream=None,
+                         events: Optional[Sequence[int]] = None) -> None:
+    lib = load_library()
+    wt = _weights_q4(qweights)
+    r = moe_routing(*(_ptr((routing or {}).get(n)) for n in
+                      ("logits", "idx", "w", "counts", "offsets", "perm", "inv")))
+    arr = None if events is None else (ctypes.c_void_p * len(events))(*events)
+    _check(lib.moe_layer_forward_q4(ctypes.byref(desc), ctypes.byref(wt), _ptr(x), _ptr(y), ctypes.byref(r),
+                                    _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream), arr), "moe_layer_forward_q4")
+
+
+def quantize_weights_q4(weights: Dict, stream=None) -> Dict:
+    """Int4 copies of a layer's expert weights (bf16 device tensors in the ABI layouts):
+    returns {name + "_codes", name + "_scales"} for every expert matrix present, plus the
+    router and bias as they are."""
+    import torch
+    out = {"w_router": weights.get("w_router"), "logit_bias": weights.get("logit_bias")}
+    for name in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+        w = weights.get(name)
+        if w is None:
+            continue
+        shape = tuple(w.shape)
+        n_mats, rows, K = (1,) + shape if len(shape) == 2 else shape
+        codes = torch.empty((n_mats, rows, K // 8), dtype=torch.int32, device=w.device)
+        scales = torch.empty((n_mats, K // 128, rows), dtype=torch.float32, device=w.device)
+        moe_quantize_q4(w, codes, scales, stream=stream)
+        out[name + "_codes"], out[name + "_scales"] = codes, scales
+    return out
+
+
 # ---------------------------------------------------------------- convenience
 class MoELayer:
     """One layer's descriptor, weights (device tensors in the ABI layouts) and workspace.
@@ -226,11 +295,14 @@ class MoELayer:
     y plus, if routing=True, the routing tensors (logits, idx, w, counts,
     offsets, perm, inv)."""
 
-    def __init__(self, desc: moe_layer_desc, weights: Dict, device=None):
+    def __init__(self, desc: moe_layer_desc, weights: Dict, device=None, qweights: Optional[Dict] = None):
+        """qweights: int4 expert weights (quantize_weights_q4); forward then runs
+        moe_layer_forward_q4."""
         import torch
         self.desc = desc
         self.weights = weights
-        ref = weights["w_up"]
+        self.qweights = qweights
+        ref = weights["w_up"] if weights.get("w_up") is not None else weights["w_router"]
         self.device = device or ref.device
         self.dtype = ref.dtype
         nbytes = moe_workspace_size(desc)
@@ -267,5 +339,8 @@ class MoELayer:
         if y is None:
             y = torch.empty((self.desc.T, self.desc.d), dtype=self.dtype, device=self.device)
         r = out_routing if out_routing is not None else (self.routing_buffers() if routing else None)
-        moe_layer_forward(self.desc, self.weights, x, y, r, self.ws, events=events)
+        if self.qweights is not None:
+            moe_layer_forward_q4(self.desc, self.qweights, x, y, r, self.ws, events=events)
+        else:
+            moe_layer_forward(self.desc, self.weights, x, y, r, self.ws, events=events)
         return (y, r) if r is not None else y

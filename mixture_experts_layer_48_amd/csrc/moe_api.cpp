@@ -241,21 +241,17 @@ moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int
     return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 
-moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
-                                   void* y, const moe_routing* routing, void* ws, size_t ws_bytes,
-                                   moe_stream_t stream, void* const* events) {
-    g_err.clear();
-    moe_status st = check_desc(desc);
-    if (st != MOE_OK) return st;
-    const moe_layer_desc& d = *desc;
-    st = check_weights(d, weights, true, true);
-    if (st != MOE_OK) return st;
+namespace {
+// The whole layer; q4 != nullptr selects the int4 expert weights (the FFN weight pointers of
+// `weights` are then ignored).
+moe_status forward_impl(const moe_layer_desc& d, const moe_weights& weights, const FfnQ4Weights* q4,
+                        const void* x, void* y, const moe_routing* routing, void* ws, size_t ws_bytes,
+                        hipStream_t s, void* const* events) {
     if (d.T == 0) return MOE_OK;
     if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x and y are required");
     const Layout L = layout_of(d);
     if (!ws || ws_bytes < L.total)
         return fail(MOE_ERR_WORKSPACE, "workspace too small for moe_layer_forward: need " + std::to_string(L.total));
-    hipStream_t s = (hipStream_t)stream;
     auto ev = [&](int i) -> hipEvent_t { return events ? (hipEvent_t)events[i] : nullptr; };
     const moe_routing none{};
     const moe_routing& R = routing ? *routing : none;
@@ -269,25 +265,111 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_weights
     void* h = at(ws, L.h);
     void* yp = at(ws, L.yp);
 
+    moe_status st;
     if ((st = record(ev(0), s)) != MOE_OK) return st;
-    st = stage_route(d, x, weights->w_router, weights->logit_bias, z, at(ws, L.h), (uint8_t*)at(ws, L.ranked),
+    st = stage_route(d, x, weights.w_router, weights.logit_bias, z, at(ws, L.h), (uint8_t*)at(ws, L.ranked),
                      idx, w, s, ev(1));
     if (st != MOE_OK) return st;
     if ((st = record(ev(2), s)) != MOE_OK) return st;
     hipError_t e = launch_permute(idx, d.T, d.k, d.N, counts, offsets, perm, inv, s);
     if (e != hipSuccess) return hip_fail(e, "permute launch");
     if ((st = record(ev(3), s)) != MOE_OK) return st;
-    FfnLaunch f = ffn_args(d, *weights, x, perm, offsets, w, h, yp);
-    f.ksplit = ksplit_of(d);
-    e = launch_ffn_in(f, s);
+    FfnLaunch f = ffn_args(d, weights, x, perm, offsets, w, h, yp);
+    if (q4) f.q4 = *q4;
+    f.ksplit = q4 ? 1 : ksplit_of(d);
+    e = q4 ? launch_ffn_in_q4(f, s) : launch_ffn_in(f, s);
     if (e != hipSuccess) return hip_fail(e, "ffn in-projection launch");
     if ((st = record(ev(4), s)) != MOE_OK) return st;
-    e = launch_ffn_out(f, s);
+    e = q4 ? launch_ffn_out_q4(f, s) : launch_ffn_out(f, s);
     if (e != hipSuccess) return hip_fail(e, "ffn out-projection launch");
     if ((st = record(ev(5), s)) != MOE_OK) return st;
     e = launch_combine(yp, inv, nullptr, y, d.T, d.k, d.d, d.has_shared, d.dtype, f.ksplit, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return record(ev(6), s);
+}
+
+moe_status check_q4(const moe_layer_desc& d, const moe_weights_q4* w, bool need_router, FfnQ4Weights* out) {
+    if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+    if (d.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "int4 expert weights need a bf16 layer");
+    if (d.d % 128 != 0 || d.d_ff % 128 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "int4 expert weights need d % 128 == 0 and d_ff % 128 == 0");
+    if (need_router && !w->w_router) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
+    auto full = [](const moe_q4_matrix& m) { return m.codes && m.scales; };
+    if (!full(w->w_up) || !full(w->w_down)) return fail(MOE_ERR_INVALID_ARG, "w_up / w_down codes or scales are NULL");
+    if (d.ffn == MOE_FFN_SWIGLU && !full(w->w_gate)) return fail(MOE_ERR_INVALID_ARG, "w_gate is NULL (SwiGLU)");
+    if (d.has_shared) {
+        if (!full(w->sh_up) || !full(w->sh_down)) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are NULL");
+        if (d.ffn == MOE_FFN_SWIGLU && !full(w->sh_gate)) return fail(MOE_ERR_INVALID_ARG, "sh_gate is NULL");
+    }
+    out->gate = w->w_gate.codes; out->gate_scales = w->w_gate.scales;
+    out->up = w->w_up.codes; out->up_scales = w->w_up.scales;
+    out->down = w->w_down.codes; out->down_scales = w->w_down.scales;
+    out->sh_gate = w->sh_gate.codes; out->sh_gate_scales = w->sh_gate.scales;
+    out->sh_up = w->sh_up.codes; out->sh_up_scales = w->sh_up.scales;
+    out->sh_down = w->sh_down.codes; out->sh_down_scales = w->sh_down.scales;
+    return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
+                                   void* y, const moe_routing* routing, void* ws, size_t ws_bytes,
+                                   moe_stream_t stream, void* const* events) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    st = check_weights(*desc, weights, true, true);
+    if (st != MOE_OK) return st;
+    return forward_impl(*desc, *weights, nullptr, x, y, routing, ws, ws_bytes, (hipStream_t)stream, events);
+}
+
+moe_status moe_layer_forward_q4(const moe_layer_desc* desc, const moe_weights_q4* weights, const void* x, void* y,
+                                const moe_routing* routing, void* ws, size_t ws_bytes, moe_stream_t stream,
+                                void* const* events) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    FfnQ4Weights q4{};
+    if ((st = check_q4(*desc, weights, true, &q4)) != MOE_OK) return st;
+    moe_weights router{};
+    router.w_router = weights->w_router;
+    router.logit_bias = weights->logit_bias;
+    return forward_impl(*desc, router, &q4, x, y, routing, ws, ws_bytes, (hipStream_t)stream, events);
+}
+
+moe_status moe_expert_ffn_q4(const moe_layer_desc* desc, const moe_weights_q4* weights, const void* x,
+                             const int32_t* perm, const int32_t* offsets, const float* row_scale, void* y_perm,
+                             void* ws, size_t ws_bytes, moe_stream_t stream) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const moe_layer_desc& d = *desc;
+    FfnQ4Weights q4{};
+    if ((st = check_q4(d, weights, false, &q4)) != MOE_OK) return st;
+    if (d.T == 0) return MOE_OK;
+    if (!x || !perm || !offsets || !y_perm) return fail(MOE_ERR_INVALID_ARG, "x, perm, offsets and y_perm are required");
+    const size_t need = ffn_ws_bytes(d);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace too small for moe_expert_ffn_q4: need " + std::to_string(need));
+    hipStream_t s = (hipStream_t)stream;
+    FfnLaunch f = ffn_args(d, moe_weights{}, x, perm, offsets, row_scale, ws, y_perm);
+    f.q4 = q4;
+    hipError_t e = launch_ffn_in_q4(f, s);
+    if (e != hipSuccess) return hip_fail(e, "ffn in-projection launch");
+    e = launch_ffn_out_q4(f, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "ffn out-projection launch");
+}
+
+moe_status moe_quantize_q4(const void* w, int32_t n_mats, int32_t rows, int32_t K, uint32_t* codes, float* scales,
+                           moe_stream_t stream) {
+    g_err.clear();
+    if (n_mats < 0 || rows < 0 || K < 0) return fail(MOE_ERR_INVALID_ARG, "negative size");
+    if (K % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "K must be a multiple of 128");
+    if ((long long)n_mats * rows * K == 0) return MOE_OK;
+    if (!w || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "w, codes and scales are required");
+    if ((long long)n_mats * rows * (K / 128) >= (1LL << 33))
+        return fail(MOE_ERR_UNSUPPORTED, "too many groups for one call");
+    hipError_t e = launch_q4_quantize(w, n_mats, rows, K, codes, scales, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "quantize launch");
 }
 
 moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_weights* weights, const void* x, void* y,

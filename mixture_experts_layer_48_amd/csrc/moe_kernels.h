@@ -20,6 +20,12 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int N, int32_t* coun
 hipError_t launch_gather_rows(const void* x, const int32_t* perm, const int32_t* offsets, int T,
                               int k, int N, int row_bytes, void* x_perm, hipStream_t s);
 
+// Int4 expert weights (codes [mats, rows, K/8] uint32, scales [mats, K/128, rows] fp32).
+struct FfnQ4Weights {
+    const uint32_t *gate, *up, *down, *sh_gate, *sh_up, *sh_down;
+    const float *gate_scales, *up_scales, *down_scales, *sh_gate_scales, *sh_up_scales, *sh_down_scales;
+};
+
 // Grouped expert FFN.  Segment e < N: rows offsets[e] .. offsets[e+1]-1, weights of expert e;
 // segment N (has_shared): rows T*k .. T*k+T-1, the shared expert's weights.
 struct FfnLaunch {
@@ -37,6 +43,7 @@ struct FfnLaunch {
     void* h;                  // [T*k + T, d_ff] hidden state
     void* y_perm;             // [ksplit][T*k + T, d] fp32 (ksplit partial sums)
     int ksplit;               // K parts of the out-projection (1 = y_perm holds the result)
+    FfnQ4Weights q4;          // int4 weights (the q4 launchers only)
 };
 int ffn_out_ksplit(int T, int k, int N, int d, int d_ff, int has_shared, int dtype);
 hipError_t launch_ffn_in(const FfnLaunch& a, hipStream_t s);   // H = act(x W_in)
@@ -61,3 +68,10 @@ hipError_t launch_ep_receive_layout(const int32_t* recv_counts, int N, int G, co
                                     int32_t* recv_perm, int32_t* recv_inv, hipStream_t s);
 hipError_t launch_ep_unpack(const void* y_grouped, const int32_t* recv_inv, const int32_t* recv_offsets, int G,
                             int max_rows, int row_bytes, void* ret, hipStream_t s);
+
+// Int4 expert weights: quantisation of n_mats bf16 matrices [rows, K] (K % 128 == 0), and the
+// weight-streaming expert FFN on int4 weights (f.q4; the out-projection always in one K part).
+hipError_t launch_q4_quantize(const void* w, long long n_mats, int rows, int K, uint32_t* codes, float* scales,
+                              hipStream_t s);
+hipError_t launch_ffn_in_q4(const FfnLaunch& f, hipStream_t s);
+hipError_t launch_ffn_out_q4(const FfnLaunch& f, hipStream_t s);

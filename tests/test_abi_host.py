@@ -170,6 +170,31 @@ def test_ep_argument_errors(lib):
     assert lib.moe_ep_unpack(4, 0, 32, None, None, None, None, None) == M.MOE_OK
 
 
+def test_q4_argument_errors(lib):
+    assert lib.moe_quantize_q4(FAKE, 2, 16, 192, FAKE, FAKE, None) == M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_q4(FAKE, 2, 16, 256, None, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_q4(None, 0, 16, 256, None, None, None) == M.MOE_OK
+    m = M.moe_q4_matrix(FAKE, FAKE)
+    none = M.moe_q4_matrix(None, None)
+    q = M.moe_weights_q4(FAKE, None, m, m, m, none, none, none)
+    r = M.moe_routing()
+    desc = _desc(d=128, d_ff=256)
+    need = M.moe_workspace_size(desc)
+    fwd = lambda d, w, ws: lib.moe_layer_forward_q4(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE,  # noqa: E731
+                                                    ctypes.byref(r), FAKE, ws, None, None)
+    assert fwd(_desc(dtype="f32", d=128, d_ff=256), q, 1 << 40) == M.MOE_ERR_UNSUPPORTED
+    assert fwd(_desc(d=192, d_ff=256), q, 1 << 40) == M.MOE_ERR_UNSUPPORTED
+    assert fwd(_desc(d=128, d_ff=320), q, 1 << 40) == M.MOE_ERR_UNSUPPORTED
+    nogate = M.moe_weights_q4(FAKE, None, none, m, m, none, none, none)
+    assert fwd(desc, nogate, need) == M.MOE_ERR_INVALID_ARG
+    half = M.moe_weights_q4(FAKE, None, m, M.moe_q4_matrix(FAKE, None), m, none, none, none)
+    assert fwd(desc, half, need) == M.MOE_ERR_INVALID_ARG
+    assert fwd(_desc(d=128, d_ff=256, has_shared=True), q, 1 << 40) == M.MOE_ERR_INVALID_ARG
+    assert fwd(desc, q, need - 1) == M.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_ffn_q4(ctypes.byref(desc), ctypes.byref(q), FAKE, FAKE, FAKE, None, FAKE, FAKE, 16,
+                                 None) == M.MOE_ERR_WORKSPACE
+
+
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define MOE_NUM_STATS (\d+)", text).group(1)) == M.MOE_NUM_STATS == len(M.STAT_NAMES)
