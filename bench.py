@@ -287,7 +287,7 @@ def main(argv=None) -> int:
         sys.stdout.write(summarize_pmc(fd, wd, int(mib) << 20, args.config, cmd))
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU's share of the layer; --gpus {args.gpus} is not "
+        print(f"bench.py: the library runs one GPU's share of the layer; --gpus {args.gpus} is not "
               f"supported (run with --gpus 1)", file=sys.stderr)
         return 2
 

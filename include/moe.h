@@ -83,7 +83,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1,   /* null required pointer, size or enum out of range */
-    MOE_ERR_UNSUPPORTED = 2,   /* valid request this build cannot run (N > 256, d % 64 on bf16) */
+    MOE_ERR_UNSUPPORTED = 2,   /* valid request the library does not support (N > 256, d % 64 on bf16) */
     MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than moe_workspace_size() or ws NULL */
     MOE_ERR_HIP = 4            /* a HIP call or kernel launch failed; see moe_last_error() */
 } moe_status;
