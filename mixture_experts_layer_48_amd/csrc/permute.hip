@@ -12,9 +12,10 @@
 //   1. each wave counts its contiguous range of slots per expert (LDS histogram per wave);
 //   2. counts, the exclusive scan over experts (offsets) and each wave's starting row per
 //      expert (offsets[e] + counts of e in earlier waves);
-//   3. each wave walks its range again in groups of 64 slots, in order; a lane's row is its
-//      wave's next free row for its expert plus the number of lower lanes with the same expert
-//      (ballot matching), so rows of an expert are in ascending slot order.
+//   3. each wave walks its range again in groups of 64 slots, in order and independently of the
+//      other waves; a lane's row is its wave's next free row for its expert plus the number of
+//      lower lanes with the same expert (ballot matching), so rows of an expert are in
+//      ascending slot order.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -131,10 +132,15 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
         } else if (valid) {
             inv[s] = -1;
         }
-        __syncthreads();  // all reads of hist done before the group's update
+        // hist[wave] is this wave's own row: its LDS reads and writes complete in program
+        // order, so the group's update needs no block barrier, only the compiler kept from
+        // moving LDS accesses across it
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
         if (e >= 0 && (eq & ~(lt | (1ull << lane))) == 0)  // highest lane of its group
             hist[wave][e] += __popcll(eq);
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
