@@ -162,6 +162,59 @@ def test_deterministic_bitwise():
     _free()
 
 
+def test_forward_on_a_side_stream():
+    # every launch goes to the stream given: a forward enqueued on a side stream (default
+    # priority), with the default stream idle and synchronised only through that stream's
+    # completion, gives the default-stream result bit for bit
+    cfg = SMALL["deepseek_small"]
+    inp = W.make_inputs(cfg, "cuda")
+    layer, y_ref, r_ref = run_layer(cfg, inp)
+    side = torch.cuda.Stream()
+    y = torch.empty_like(y_ref)
+    r = layer.routing_buffers()
+    torch.cuda.synchronize()
+    M.moe_layer_forward(layer.desc, inp, inp["x"], y, r, layer.ws, stream=side)
+    side.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    for key in ("idx", "counts", "perm", "inv"):
+        assert torch.equal(r[key], r_ref[key]), key
+    _free()
+
+
+def test_forward_in_a_captured_graph():
+    # the library allocates, clears and synchronises nothing, so a whole forward can be captured
+    # into one graph; replays (with eager work and synchronisations between them) must all give
+    # the eager result bit for bit
+    for cfg in (SMALL["skewed_small"], SMALL["mixtral_decode_small"]):
+        log(f"[graph] {cfg.name}")
+        inp = W.make_inputs(cfg, "cuda")
+        layer, y_ref, r_ref = run_layer(cfg, inp)
+        y = torch.empty_like(y_ref)
+        r = layer.routing_buffers()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                M.moe_layer_forward(layer.desc, inp, inp["x"], y, r, layer.ws)
+        torch.cuda.synchronize()
+        for rep in range(4):
+            y.zero_()
+            r["perm"].fill_(-7)
+            layer.forward(inp["x"])                       # eager work between the replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y,
+                               y_ref.view(torch.int16) if y_ref.dtype == torch.bfloat16 else y_ref), rep
+            for key in ("idx", "w", "counts", "offsets", "inv"):
+                assert torch.equal(r[key], r_ref[key]), (rep, key)
+            n = int(r_ref["offsets"][-1])
+            assert torch.equal(r["perm"][:n], r_ref["perm"][:n]), rep
+        del g
+    _free()
+
+
 def test_stage_entry_points_compose_to_forward():
     for cfg in (SMALL["deepseek_small"], SMALL["skewed_small"], SMALL["swiglu_f32_shared"]):
         log(f"[stages] {cfg.name}")
