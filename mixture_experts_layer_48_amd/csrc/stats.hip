@@ -26,7 +26,7 @@ constexpr int ST_MAX_BLOCKS = 256;
 constexpr int ST_BATCH = 2;              // token passes whose inputs a wave loads before using them
 constexpr int FIN_THREADS = 1024;
 constexpr int FIN_GROUPS = FIN_THREADS / MOE_MAX_EXPERTS;
-constexpr int FIN_UNROLL = 32;           // partial sums in flight per thread
+constexpr int FIN_UNROLL = 8;            // partial sums in flight per thread
 
 __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
     const uint64_t u = (uint64_t)__double_as_longlong(v);
