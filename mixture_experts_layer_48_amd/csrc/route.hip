@@ -275,7 +275,8 @@ __global__ __launch_bounds__(64) void rank_sort_kernel(const float* __restrict__
 // or before the rank the token resumes from; picks are shallow (on the skewed layer every pick
 // is within 41 ranks), and a scan that runs past the window reads the list from memory.  The
 // window keeps a chunk at one token per thread.  "Room at chunk start" is a byte table in LDS
-// and "already held" is in registers, so a token steps over full experts cheaply.  Proposal
+// and "already held" is in registers; a scan takes 16 ranks at a time, so a token steps over
+// full experts cheaply.  Proposal
 // counts are per wave, stamped with the round number, so no round has to clear them.
 #define CAP_THREADS 1024
 #define CAP_WIN 4                   // 16-byte pieces (16 ranks each) in a token's window
@@ -359,32 +360,56 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                 ++round;
                 if (choose) {                             // next candidate from (q, bpos) on
                     choice = -1;
-                    while (q < NQ) {
-                        const int wi = q - wq0;             // >= 0: the scan starts in the window
-                        const uint32_t wd = wi < WW ? rk4[wi * CT + tid]
-                                                    : *(const uint32_t*)(ranked + (size_t)t * NP + 4 * q);
-                        // room flags of the word's four experts, one bit each
-                        const uint32_t rf = (uint32_t)roomb[wd & 0xFF] | ((uint32_t)roomb[(wd >> 8) & 0xFF] << 1) |
-                                            ((uint32_t)roomb[(wd >> 16) & 0xFF] << 2) |
-                                            ((uint32_t)roomb[wd >> 24] << 3);
-                        if ((rf >> bpos) == 0) {                              // nothing left here
-                            ++q;
-                            bpos = 0;
-                            continue;
-                        }
-                        for (; bpos < 4; ++bpos) {
-                            const int e = (wd >> (8 * bpos)) & 0xFF;
-                            if (!((rf >> bpos) & 1u)) continue;              // full at chunk start
+                    // one aligned piece of four words (16 ranks) at a time: the words, then the
+                    // room flags of their 16 experts, each read at once, so a scan over full
+                    // experts waits for two LDS reads per 16 ranks
+                    auto piece = [&](const uint32_t (&wd)[4], int q0) {
+                        // all 16 reads unconditional (any byte indexes the table), so that they go
+                        // out together; words past the row's end are masked afterwards
+                        uint32_t rf = 0;                    // bit 4 i + b: word i, byte b had room
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                rf |= (uint32_t)roomb[(wd[i] >> (8 * b)) & 0xFF] << (4 * i + b);
+                        if (NQ - q0 < 4) rf &= (1u << (4 * (NQ - q0))) - 1u;
+                        rf &= ~0u << (4 * (q - q0) + bpos);    // ranks before the resume point
+                        while (rf) {
+                            const int p = __builtin_ctz(rf);
+                            rf &= rf - 1;
+                            const uint32_t w = (p >> 2) == 0 ? wd[0] : (p >> 2) == 1 ? wd[1]
+                                             : (p >> 2) == 2 ? wd[2] : wd[3];
+                            const int e = (w >> (8 * (p & 3))) & 0xFF;
                             if (t > tau[e]) continue;                         // turned away this chunk
                             bool held = e == h0 || e == h1 || e == h2 || e == h3;
                             for (int jj = 4; jj < j && !held; ++jj) held = idx[(size_t)t * k + jj] == e;
                             if (held) continue;
                             choice = e;
-                            break;
+                            q = q0 + (p >> 2);
+                            bpos = p & 3;
+                            return true;
                         }
-                        if (choice >= 0) break;
-                        ++q;
+                        q = q0 + 4;
                         bpos = 0;
+                        return false;
+                    };
+                    // inside the window (it starts on a piece boundary): LDS reads only, so no
+                    // wait for the next chunk's loads still in flight
+                    while (q < NQ && (q & ~3) - wq0 < WW) {
+                        const int q0 = q & ~3;
+                        uint32_t wd[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) wd[i] = rk4[(q0 + i - wq0) * CT + tid];   // in the window array
+                        if (piece(wd, q0)) break;
+                    }
+                    // past the window (rare): the rest of the ranked row from memory
+                    while (choice < 0 && q < NQ) {
+                        const int q0 = q & ~3;
+                        uint32_t wd[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            wd[i] = q0 + i < NQ ? *(const uint32_t*)(ranked + (size_t)t * NP + 4 * (q0 + i)) : 0u;
+                        if (piece(wd, q0)) break;
                     }
                     choose = false;
                 }
