@@ -421,11 +421,15 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                 __syncthreads();
                 bool rejected = false;
                 if (choice >= 0) {
+                    // proposals to the same expert from earlier waves: every wave's count read at
+                    // once, then the earlier ones added
+                    uint32_t cw[CAP_WAVES_];
+#pragma unroll
+                    for (int ww = 0; ww < CAP_WAVES_; ++ww) cw[ww] = cnt[ww][choice];
                     int rank = rin;
-                    for (int ww = 0; ww < wave; ++ww) {
-                        const uint32_t c = cnt[ww][choice];
-                        rank += (c >> 16) == round ? (int)(c & 0xFFFF) : 0;
-                    }
+#pragma unroll
+                    for (int ww = 0; ww < CAP_WAVES_; ++ww)
+                        rank += (ww < wave && (cw[ww] >> 16) == round) ? (int)(cw[ww] & 0xFFFF) : 0;
                     const int room = C - fill[choice];
                     if (rank == room - 1) tau[choice] = t;
                     if (rank >= room) {
