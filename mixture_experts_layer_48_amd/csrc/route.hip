@@ -7,6 +7,8 @@
 // "大模型MoE混合专家架构原理与DeepSeek-V4工程实践解析", section MoE核心机制).
 // Capacity: a full expert passes the token on to its next-best expert (page "MoE稀疏激活原理与
 // 工程实践", section 2.2).
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -47,83 +49,94 @@ size_t router_workspace_bytes(int T, int d, int N, int dtype) {
     return r.ks > 1 ? (size_t)r.ks * T * N * sizeof(double) : 0;
 }
 
-// NS k-steps of 32: all loads first, then the MFMAs.
-template <int NS>
-__device__ __forceinline__ void router_steps(const bf16* pa0, const bf16* pa1, const bf16* const (&pb)[4],
-                                             bool okA0, bool okA1, const bool (&okB)[4], int nct, int kk,
-                                             f32x4 (&acc)[4][2]) {
-    const bf16x8 zero8 = {};
-    bf16x8 a0[NS], a1[NS], bv[NS][4];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        a0[s] = okA0 ? *(const bf16x8*)(pa0 + kk + 32 * s) : zero8;
-        a1[s] = okA1 ? *(const bf16x8*)(pa1 + kk + 32 * s) : zero8;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (c < nct) bv[s][c] = okB[c] ? *(const bf16x8*)(pb[c] + kk + 32 * s) : zero8;
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (c < nct) {
-                acc[c][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[s], bv[s][c], acc[c][0], 0, 0, 0);
-                acc[c][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[s], bv[s][c], acc[c][1], 0, 0, 0);
-            }
-}
-
+// One wave: NCT column tiles of 16 experts (NCT = 4 except on a partial last expert tile) of
+// its expert tile, for tokens t0 .. t0 + 31, over its K part.  Rows past T and experts past N
+// load clamped (valid) addresses and their results are never stored, so every load is
+// unconditional and the wait counts stay exact: the fragments of the next 32-input step are
+// loaded while the current step's MFMAs run.
+template <int NCT>
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ wr, const float* __restrict__ bias,
-    float* __restrict__ z, double* __restrict__ part, int T, int d, int N, RouterSplit sp) {
+    float* __restrict__ z, double* __restrict__ part, int T, int d, int N, RouterSplit sp, int et_beg,
+    int n_et) {
     const int lane = threadIdx.x & 63;
     const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int et = u % sp.n_et, rest = u / sp.n_et;
+    const int et = et_beg + u % n_et, rest = u / n_et;
     const int kp = rest % sp.ks, tt = rest / sp.ks;
     if (tt >= sp.n_tt) return;
     const int t0 = tt * RL_BM, e0 = et * RL_BN;
-    const int nct = min(4, (N - e0 + 15) >> 4);   // valid 16-wide column tiles (uniform)
     const int koff = (lane >> 4) * 8;
     const int rowA0 = t0 + (lane & 15), rowA1 = rowA0 + 16;
-    const bool okA0 = rowA0 < T, okA1 = rowA1 < T;
-    const bf16* pa0 = x + (size_t)(okA0 ? rowA0 : 0) * d + koff;
-    const bf16* pa1 = x + (size_t)(okA1 ? rowA1 : 0) * d + koff;
-    const bf16* pb[4];
-    bool okB[4];
+    const bf16* pa0 = x + (size_t)(rowA0 < T ? rowA0 : 0) * d + koff;
+    const bf16* pa1 = x + (size_t)(rowA1 < T ? rowA1 : 0) * d + koff;
+    const bf16* pb[NCT];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        int e = e0 + c * 16 + (lane & 15);
-        okB[c] = (c < nct) && (e < N);
-        pb[c] = wr + (size_t)(okB[c] ? e : 0) * d + koff;
+    for (int c = 0; c < NCT; ++c) {
+        const int e = e0 + c * 16 + (lane & 15);
+        pb[c] = wr + (size_t)(e < N ? e : 0) * d + koff;
     }
-    double acc64[4][2][4];
+    double acc64[NCT][2][4];
+    f32x4 acc[NCT][2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NCT; ++c)
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < 2; ++r) {
+            acc[c][r] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc64[c][r][i] = 0.0;
-
-    const int c_beg = kp * sp.cpp, c_end = min(c_beg + sp.cpp, sp.nchunks);
-    for (int ch = c_beg; ch < c_end; ++ch) {
-        const int kc = ch * RL_CHUNK, kend = min(kc + RL_CHUNK, d);
-        f32x4 acc[4][2];
+        }
+    struct Frag {
+        bf16x8 a0, a1, b[NCT];
+    };
+    auto load = [&](Frag& f, int k) {
+        f.a0 = *(const bf16x8*)(pa0 + k);
+        f.a1 = *(const bf16x8*)(pa1 + k);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c][0] = acc[c][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        int kk = kc;
-        for (; kk + 64 <= kend; kk += 64) router_steps<2>(pa0, pa1, pb, okA0, okA1, okB, nct, kk, acc);
-        for (; kk < kend; kk += 32) router_steps<1>(pa0, pa1, pb, okA0, okA1, okB, nct, kk, acc);
+        for (int c = 0; c < NCT; ++c) f.b[c] = *(const bf16x8*)(pb[c] + k);
+    };
+    auto mma = [&](const Frag& f) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < NCT; ++c) {
+            acc[c][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a0, f.b[c], acc[c][0], 0, 0, 0);
+            acc[c][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a1, f.b[c], acc[c][1], 0, 0, 0);
+        }
+    };
+    // the fp32 sum of a chunk of RL_CHUNK inputs goes into the fp64 sum, in chunk order
+    auto fold = [&]() {
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc64[c][r][i] += (double)acc[c][r][i];
+                acc[c][r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+    };
+    constexpr int SPC = RL_CHUNK / 32;            // 32-input steps per chunk
+    const int kbeg = kp * sp.cpp * RL_CHUNK;
+    const int kend = min(kbeg + sp.cpp * RL_CHUNK, d);
+    const int nsteps = (kend - kbeg) / 32;        // d % 64 == 0 for bf16 layers
+    Frag f0, f1;
+    load(f0, kbeg);
+    int st = 0;
+    for (; st + 2 <= nsteps; st += 2) {
+        load(f1, kbeg + 32 * (st + 1));
+        mma(f0);
+        if ((st + 1) % SPC == 0) fold();
+        if (st + 2 < nsteps) load(f0, kbeg + 32 * (st + 2));
+        mma(f1);
+        if ((st + 2) % SPC == 0) fold();
     }
+    if (st < nsteps) {
+        mma(f0);
+        ++st;
+    }
+    if (st % SPC != 0) fold();                   // a last, shorter chunk
     // C layout of 16x16 MFMA: lane holds column (lane & 15), rows 4*(lane >> 4) + i.
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NCT; ++c) {
         const int e = e0 + c * 16 + (lane & 15);
-        if (c >= nct || e >= N) continue;
+        if (e >= N) continue;
         const double b = bias ? (double)bias[e] : 0.0;
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -503,9 +516,22 @@ hipError_t launch_router_logits(const void* x, const void* wr, const float* bias
     if (T == 0) return hipSuccess;
     if (dtype == 1) {
         const RouterSplit sp = router_split(T, d, N);
-        const long long units = (long long)sp.n_tt * sp.n_et * sp.ks;
-        hipLaunchKernelGGL(router_logits_bf16_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s,
-                           (const bf16*)x, (const bf16*)wr, bias, z, (double*)ws, T, d, N, sp);
+        // full expert tiles (4 column tiles of 16) in one launch, a partial last tile in another
+        const int n_full = N / RL_BN, last_nct = ((N % RL_BN) + 15) / 16;
+        auto launch = [&](auto nct, int et_beg, int n_et) {
+            const long long units = (long long)sp.n_tt * n_et * sp.ks;
+            hipLaunchKernelGGL(router_logits_bf16_kernel<decltype(nct)::value>, dim3((unsigned)((units + 3) / 4)),
+                               dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, bias, z, (double*)ws, T, d, N,
+                               sp, et_beg, n_et);
+        };
+        if (n_full > 0) launch(std::integral_constant<int, 4>{}, 0, n_full);
+        switch (last_nct) {
+            case 1: launch(std::integral_constant<int, 1>{}, n_full, 1); break;
+            case 2: launch(std::integral_constant<int, 2>{}, n_full, 1); break;
+            case 3: launch(std::integral_constant<int, 3>{}, n_full, 1); break;
+            case 4: launch(std::integral_constant<int, 4>{}, n_full, 1); break;
+            default: break;
+        }
         if (sp.ks > 1) {
             const long long n = (long long)T * N;
             hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
