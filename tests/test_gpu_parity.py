@@ -148,6 +148,24 @@ def test_all_tokens_to_one_expert():
     _free()
 
 
+def test_large_batch():
+    # 262144 tokens x top-2: half a million slots through the single-block grouping, the
+    # router and the combine at scale (int32 row indexing well away from its limit)
+    cfg = W.LayerConfig("large_batch", T=262144, d=64, N=16, k=2, d_ff=64, dtype="bf16", ffn=W.FFN_SWIGLU,
+                        gating=W.GATE_TOPK_SOFTMAX, seed=26)
+    inp = W.make_inputs(cfg, "cuda")
+    layer, y, r = run_layer(cfg, inp)
+    rn = routing_to_np(r)
+    z64, zerr, alike = check_routing(cfg, inp, rn)
+    rng = np.random.default_rng(cfg.seed)
+    pool = np.nonzero(alike)[0]
+    tokens = np.sort(np.concatenate([rng.choice(pool, size=32, replace=False), pool[-4:]]))
+    ref = oracle_forward(cfg, inp, tokens=tokens, z=z64)
+    check_y(cfg, f64(y)[tokens], ref["y"], label=" sampled tokens:")
+    del layer, y, r, inp
+    _free()
+
+
 def test_deterministic_bitwise():
     for cfg in (SMALL["deepseek_small"], SMALL["skewed_small"], SMALL["mixtral_small"]):
         log(f"[determinism] {cfg.name}")
