@@ -72,7 +72,3 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // u -> -inf the reciprocal of +inf is 0 and the result -0.
 __device__ __forceinline__ float silu_f32(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
 
-// Host-side launch status helper.
-struct LaunchCheck {
-    static hipError_t last() { return hipGetLastError(); }
-};
