@@ -21,6 +21,7 @@ import math
 import os
 import re
 import sys
+import statistics
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -341,7 +342,8 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     stage_ms = [sum(hip.elapsed_ms(ev[s], ev[s + 1]) for ev in events) / args.steps
                 for s in range(M.MOE_NUM_STAGES)]
-    step_dev_ms = sum(hip.elapsed_ms(ev[0], ev[-1]) for ev in events) / args.steps
+    step_dev = sorted(hip.elapsed_ms(ev[0], ev[-1]) for ev in events)
+    step_dev_ms = sum(step_dev) / args.steps
     # Routing statistics of the same routing (outside the layer step): device time per call
     # between two events around `steps` back-to-back calls.
     st_out = None
@@ -405,7 +407,12 @@ def main(argv=None) -> int:
                   "mfma_frac": alg["flops"] / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "gbs_distinct_experts": alg["bytes"] / (ms_per_step * 1e-3) / 1e9,
                   "hbm_frac": alg["bytes"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                  "experts_touched": alg["touched"], "device_ms_per_step": step_dev_ms},
+                  "experts_touched": alg["touched"], "device_ms_per_step": step_dev_ms,
+                  "device_ms_median": statistics.median(step_dev), "device_ms_min": step_dev[0],
+                  # the time the binding roofline allows, max(flops / MFMA peak, bytes / HBM peak),
+                  # over the measured time
+                  "roofline_time_frac": max(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12),
+                                            alg["bytes"] / (PEAK_HBM_GBS * 1e9)) / (ms_per_step * 1e-3)},
         "stages_ms": dict(zip(M.STAGE_NAMES, stage_ms)),
         "routing_stats": routing_stats,
         "ep_layout": ep_layout,

@@ -73,6 +73,11 @@ SMALL = {
                                         ffn=W.FFN_RELU2, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=22),
     "tiles256_ragged_cols": W.LayerConfig("tiles256_ragged_cols", T=300, d=256, N=1, k=1, d_ff=448, dtype="bf16",
                                         ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=23),
+    # about 256 rows per expert (195-298): many experts are a full 256-row tile plus a short one,
+    # and there are more tiles than resident blocks, so blocks run several tiles in a row and each
+    # tile's last stages load the next tile's first ones; every token is checked
+    "multi_tile_blocks": W.LayerConfig("multi_tile_blocks", T=4096, d=512, N=32, k=2, d_ff=1024, dtype="bf16",
+                                       ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=27),
     # capacity with 256 experts: scans that run past the ranked-list window kept in LDS (picks
     # deeper than 64 ranks), with slots dropped once every expert is full, and without drops
     "capacity_deep_drops": W.LayerConfig("capacity_deep_drops", T=300, d=64, N=256, k=2, d_ff=64, dtype="bf16",
