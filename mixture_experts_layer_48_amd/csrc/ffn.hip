@@ -10,8 +10,8 @@
 // worst case (sum over experts of ceil(rows/BM) <= ceil(T*k/BM) + N); each block finds its
 // segment and m-tile on the device from offsets, so the host never reads the routing.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, block tiles of 256 or 128 rows, K step 64, LDS double
-// buffer filled by direct loads, 4 waves each owning a quarter of the tile.  The in-projection gathers its A
+// bf16 path: v_mfma_f32_32x32x16_bf16, block tiles of 128, 256 or 320 rows, K step 64, LDS
+// double buffer filled by direct loads, 4 or 8 waves each owning an equal part of the tile.  The in-projection gathers its A
 // rows straight from x (row = token of the slot), so the permuted copy of x is never built;
 // SwiGLU (silu(g) * u) or ReLU is applied in registers and H is stored in bf16.  The
 // out-projection multiplies each row by its slot's gate weight and stores the row in fp32, so the
@@ -90,14 +90,22 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, lds_void_t* 
 // next to an expert's short last one) does not fall on the same blocks every round.
 #define FFN_MAX_SEG 320   // 5 segments per lane of one wave: routed experts and the shared one
 
+// Sub-tiles per wave of the variant a tile with nsub valid 32-row sub-tiles runs: the fewest of
+// 1, 2, 4 (when below TM) and TM that holds them.
+template <int TM, int WGM>
+__device__ __forceinline__ int variant_nv(int nsub) {
+    if (TM >= 2 && nsub <= WGM) return 1;
+    if (TM >= 4 && nsub <= 2 * WGM) return 2;
+    if (TM >= 5 && nsub <= 4 * WGM) return 4;
+    return TM;
+}
+
 // Estimated cost of a tile in 1/256 of a full tile: a short tile (an expert's last m-tile) runs
 // the variant with fewer sub-tiles per wave and costs about half a full tile plus its share of
 // the MFMAs (measured: a 64-row tile of 256 takes 0.65 of a full one).
 template <int TM, int WGM>
 __device__ __forceinline__ int tile_cost(int rows_in_tile) {
-    const int nsub = (rows_in_tile + 31) / 32;
-    const int nv = (TM >= 2 && nsub <= WGM) ? 1 : (TM >= 4 && nsub <= 2 * WGM) ? 2 : TM;
-    return 128 + 128 * nv / TM;
+    return 128 + 128 * variant_nv<TM, WGM>((rows_in_tile + 31) / 32) / TM;
 }
 
 template <int BM, int TM, int WGM>
@@ -390,6 +398,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     // during step 0; the first part holds A rows only, so that a tile's last two stages can
     // switch the A offsets to the next tile before the B offsets
     constexpr int NLD0 = (NLD + 1) / 2 < A_INS ? (NLD + 1) / 2 : A_INS;
+    static_assert(NLD0 == A_INS, "the second part of a stage's loads holds B rows only");
     // Interleave one MFMA with the step's other instructions so that a single wave per SIMD keeps
     // the matrix core busy: MFMA, fragment read, MFMA, load, ...
     auto interleave = [&](int n_ds, int n_ld, auto nv) {
@@ -583,9 +592,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         }
     };
     auto run_tile = [&]() {
-        const int nsub = (cur.row_end - (cur.row_beg + cur.mt * BM) + 31) / 32;
-        if (TM >= 2 && nsub <= WGM) run(std::integral_constant<int, 1>{});
-        else if (TM >= 4 && nsub <= 2 * WGM) run(std::integral_constant<int, 2>{});
+        const int nv = variant_nv<TM, WGM>((cur.row_end - (cur.row_beg + cur.mt * BM) + 31) / 32);
+        if (TM >= 2 && nv == 1) run(std::integral_constant<int, 1>{});
+        else if (TM >= 4 && nv == 2) run(std::integral_constant<int, 2>{});
+        else if (TM >= 5 && nv == 4) run(std::integral_constant<int, (TM >= 5 ? 4 : TM)>{});
         else run(std::integral_constant<int, TM>{});
     };
 
@@ -862,6 +872,18 @@ static bool big_tiles(const FfnLaunch& f) {
     return (long long)f.T * f.k >= 192LL * f.N;   // >= 192 rows per expert on average
 }
 
+// 320-row in-projection tiles (eight waves, 2 x 4) when experts hold 224 to 288 rows on
+// average: an expert of 257 to 320 rows is then one m-tile instead of a full 256-row tile plus a
+// short one that streams the expert's whole weight matrix a second time.  Measured on one box
+// against 256-row tiles, gate/up projection: DeepSeek-V3 shape 4.22 vs 5.10 ms, top-1 over 16
+// experts 1.05 vs 1.17, shared + top-7 of 256 3.94 vs 4.09, skewed with capacity 1.50 vs 1.53.
+// (320 x 128 with four waves needs 320 accumulator registers per lane and spills; 320 x 64
+// with four waves fits but was slower than 256-row tiles on all four.)
+static bool tiles_320(const FfnLaunch& f) {
+    const long long rows = (long long)f.T * f.k;
+    return rows >= 224LL * f.N && rows <= 288LL * f.N;
+}
+
 // K parts for the out-projection: two when its K is long and one part alone would leave the
 // last round of blocks on the CUs mostly empty.  The parts' fp32 outputs are summed, in order,
 // by the combine.
@@ -890,6 +912,7 @@ hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
             a.B0 = (const bf16*)f.w_gate; a.B1 = (const bf16*)f.w_up;
             a.S0 = (const bf16*)f.sh_gate; a.S1 = (const bf16*)f.sh_up;
             if (skinny(f)) return launch_skinny<MODE_IN_SWIGLU, SK_U_IN, SK_CG_IN>(a, s);
+            if (tiles_320(f)) return launch_bf16<MODE_IN_SWIGLU, 320, 128, 2, 4>(a, s);
             if (big_tiles(f)) return launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, s);
             return launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, s);
         }

@@ -73,10 +73,18 @@ SMALL = {
                                         ffn=W.FFN_RELU2, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=22),
     "tiles256_ragged_cols": W.LayerConfig("tiles256_ragged_cols", T=300, d=256, N=1, k=1, d_ff=448, dtype="bf16",
                                         ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=23),
-    # about 256 rows per expert (195-298): many experts are a full 256-row tile plus a short one,
-    # and there are more tiles than resident blocks, so blocks run several tiles in a row and each
-    # tile's last stages load the next tile's first ones; every token is checked
-    "multi_tile_blocks": W.LayerConfig("multi_tile_blocks", T=4096, d=512, N=32, k=2, d_ff=1024, dtype="bf16",
+    # 224-288 rows per expert on average: 320-row in-projection tiles.  Loads 253/255/255/277
+    # and a 520-row shared expert (a 320-row and a 200-row tile); then skewed loads
+    # 982/638/271/92/32/9/21/3 (full 320-row tiles, a 318-row one, 96-, 64- and 32-row ones)
+    "tiles320_swiglu_shared": W.LayerConfig("tiles320_swiglu_shared", T=520, d=256, N=4, k=2, d_ff=320,
+                                            dtype="bf16", ffn=W.FFN_SWIGLU, gating=W.GATE_SOFTMAX_TOPK,
+                                            has_shared=True, seed=24),
+    "tiles320_skewed": W.LayerConfig("tiles320_skewed", T=1024, d=128, N=8, k=2, d_ff=192, dtype="bf16",
+                                     ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, zipf_bias=True, seed=25),
+    # about 256 rows per expert (195-298, 320-row tiles), more tiles than resident blocks: blocks
+    # run several tiles in a row and each tile's last stages load the next tile's first ones;
+    # every token is checked
+    "multi_tile_blocks": W.LayerConfig("multi_tile_blocks", T=4096, d=512, N=32, k=2, d_ff=2048, dtype="bf16",
                                        ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=27),
     # capacity with 256 experts: scans that run past the ranked-list window kept in LDS (picks
     # deeper than 64 ranks), with slots dropped once every expert is full, and without drops
