@@ -883,6 +883,14 @@ static bool tiles_320(const FfnLaunch& f) {
     const long long rows = (long long)f.T * f.k;
     return rows >= 224LL * f.N && rows <= 288LL * f.N;
 }
+// The same for the out-projection (320 x 256, eight waves), from 240 rows per expert on average:
+// down projection 2.55 vs 2.84 ms on the DeepSeek-V3 shape, 0.65 vs 0.72 on top-1 over 16
+// experts, 0.85 vs 0.89 on the skewed layer; at 224 rows per expert (shared + top-7 of 256),
+// where few experts pass 256 rows, 2.48 vs 2.44.
+static bool tiles_320_out(const FfnLaunch& f) {
+    const long long rows = (long long)f.T * f.k;
+    return rows >= 240LL * f.N && rows <= 288LL * f.N;
+}
 
 // K parts for the out-projection: two when its K is long and one part alone would leave the
 // last round of blocks on the CUs mostly empty.  The parts' fp32 outputs are summed, in order,
@@ -954,6 +962,7 @@ hipError_t launch_ffn_out(const FfnLaunch& f, hipStream_t s) {
         // eight waves (2 x 4, two per SIMD) for the out-projection: measured on the same box,
         // Mixtral down projection 0.94 vs 1.01 ms with four, skewed 0.89 vs 0.93, DeepSeek-V3
         // 2.72 vs 2.71; four stay faster for the SwiGLU in-projection (1.70 vs 1.59 ms)
+        if (tiles_320_out(f)) return launch_bf16<MODE_OUT, 320, 256, 2, 4>(a, s);
         if (big_tiles(f)) return launch_bf16<MODE_OUT, 256, 256, 2, 4>(a, s);
         return launch_bf16<MODE_OUT, 128, 128, 2, 2>(a, s);
     }

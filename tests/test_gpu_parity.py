@@ -81,6 +81,9 @@ SMALL = {
                                             has_shared=True, seed=24),
     "tiles320_skewed": W.LayerConfig("tiles320_skewed", T=1024, d=128, N=8, k=2, d_ff=192, dtype="bf16",
                                      ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, zipf_bias=True, seed=25),
+    # 320-row out-projection tiles with the long K split in two parts
+    "split_k_tiles320": W.LayerConfig("split_k_tiles320", T=256, d=128, N=2, k=2, d_ff=8192, dtype="bf16",
+                                      ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=28),
     # about 256 rows per expert (195-298, 320-row tiles), more tiles than resident blocks: blocks
     # run several tiles in a row and each tile's last stages load the next tile's first ones;
     # every token is checked
