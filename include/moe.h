@@ -67,8 +67,9 @@
  *    counts.  In y_perm its output for token t sits at row T*k + t.
  *
  * Limits: 1 <= k <= N <= 256; T >= 0 (T = 0 is a no-op); d, d_ff >= 1.  For MOE_BF16:
- *   d % 64 == 0 and d_ff % 64 == 0 (else MOE_ERR_UNSUPPORTED).  MOE_F32 has no divisibility
- *   requirement.  T * k must fit in int32 with T*k + T + 1 < 2^31.
+ *   d % 64 == 0 and d_ff % 64 == 0, and x at most 4 GiB: T * d * 2 < 2^32 bytes (else
+ *   MOE_ERR_UNSUPPORTED).  MOE_F32 has no divisibility requirement.  T * k must fit in int32
+ *   with T*k + T + 1 < 2^31.
  */
 #ifndef MOE_H_
 #define MOE_H_

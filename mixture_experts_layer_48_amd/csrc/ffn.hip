@@ -301,10 +301,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     // the LDS slots they free, when the next tile starts in slot 0 (an even stage count).
     const bool chain = (KT % 2 == 0) && KT >= 4;
     const size_t wstride = (size_t)a.Ncols * a.K;
-    const char* baseA = (const char*)a.A;
+    // Base of the A loads: x for the in-projection, whose gathered rows may sit anywhere in it;
+    // the tile's first row of H for the out-projection, whose rows are contiguous per tile, so
+    // that H may exceed the 4 GiB of a 32-bit offset.
+    auto base_a = [&](const TileInfo& ti) -> const char* {
+        if (MODE != MODE_OUT) return (const char*)a.A;
+        return uniform_ptr((const char*)(a.A + (size_t)(ti.row_beg + ti.mt * BM) * a.K));
+    };
+    const char* baseA = base_a(cur);
 
     // per-lane 32-bit byte offsets of this wave's load instructions from a uniform base
-    // (x / H stay below 4 GiB, one expert's weight matrix too)
+    // (x stays below 4 GiB, which the host checks; one tile of H and one expert's weight
+    // matrix do too)
     // Lane-derived values are recomputed where a tile's offsets are set (an empty asm hides the
     // lane id from the optimiser there), instead of being precomputed once per row group and
     // held in registers for the whole kernel.
@@ -321,8 +329,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         const int m0 = ti.row_beg + ti.mt * BM, rl = 8 * (wave + NW * i) + (l >> 3);
         return (m0 + rl < ti.row_end) ? m0 + rl : m0;
     };
-    auto a_src = [&](const TileInfo& ti, int r) {        // x row of slot row r (in-projection)
-        if (MODE == MODE_OUT) return r;
+    // in-projection: x row of slot row r; out-projection: r's place in its tile
+    auto a_src = [&](const TileInfo& ti, int r) {
+        if (MODE == MODE_OUT) return r - (ti.row_beg + ti.mt * BM);
         return (ti.seg < a.N) ? a.perm[r] / a.k : r - a.T * a.k;
     };
     uint32_t offA[A_INS], offB[B_INS];
@@ -349,6 +358,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
 #pragma unroll
         for (int i = 0; i < A_INS; ++i)
             offA[i] = ((uint32_t)a_src(ti, a_row(ti, i, l)) * (uint32_t)a.K + lc) * 2u;
+        baseA = base_a(ti);
     };
     auto scale_of = [&](const TileInfo& ti) {            // gate weight of this thread's row
         const int r = ti.row_beg + ti.mt * BM + tid;
@@ -489,9 +499,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         const uint32_t lc = (uint32_t)(((l & 7) ^ ((4 * wave + (l >> 4)) & 7)) * 8);
 #pragma unroll
         for (int i = 0; i < A_INS; ++i) {
-            const int src = (MODE == MODE_OUT) ? a_row(nx, i, l) : s_src[8 * (wave + NW * i) + (l >> 3)];
+            const int src = (MODE == MODE_OUT) ? a_src(nx, a_row(nx, i, l)) : s_src[8 * (wave + NW * i) + (l >> 3)];
             offA[i] = ((uint32_t)src * (uint32_t)a.K + lc) * 2u;
         }
+        baseA = base_a(nx);
     };
 
     // Epilogue (transposed accumulator layout, see mfmas): per sub-tile one row per lane and

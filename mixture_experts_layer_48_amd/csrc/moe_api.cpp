@@ -59,6 +59,9 @@ moe_status check_desc(const moe_layer_desc* d) {
         return fail(MOE_ERR_UNSUPPORTED, "T*k + T exceeds int32 row indexing");
     if ((long long)d->T * d->d >= (long long)INT_MAX * 64LL)
         return fail(MOE_ERR_UNSUPPORTED, "T*d too large");
+    // the grouped GEMM gathers x rows through 32-bit byte offsets from one base
+    if (d->dtype == MOE_BF16 && (long long)d->T * d->d * 2 >= (1LL << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "bf16 x larger than 4 GiB (T*d*2 >= 2^32)");
     return MOE_OK;
 }
 

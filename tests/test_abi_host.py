@@ -55,6 +55,13 @@ def test_workspace_size_grows_with_tokens_and_is_zero_when_invalid():
     assert cap >= a + 128 * 8           # ranked expert lists
 
 
+def test_x_size_limit_applies_to_bf16_only():
+    # the grouped GEMM addresses x with 32-bit byte offsets: bf16 x must stay below 4 GiB
+    assert M.moe_workspace_size(_desc(T=(1 << 19) - 1, d=4096)) > 0
+    assert M.moe_workspace_size(_desc(T=1 << 19, d=4096)) == 0
+    assert M.moe_workspace_size(_desc(T=1 << 19, d=4096, dtype="f32")) > 0
+
+
 FAKE = 0x1000   # never dereferenced: every call below fails validation on the host
 
 
@@ -71,6 +78,7 @@ FAKE = 0x1000   # never dereferenced: every call below fails validation on the h
     (dict(N=300, k=2), M.MOE_ERR_UNSUPPORTED),
     (dict(d=100), M.MOE_ERR_UNSUPPORTED),
     (dict(d_ff=200), M.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 19, d=4096), M.MOE_ERR_UNSUPPORTED),     # bf16 x of exactly 4 GiB
 ])
 def test_descriptor_errors(lib, kw, status):
     desc = _desc(**kw)

@@ -293,6 +293,28 @@ SAMPLE_TOKENS = {"mixtral_prefill": 8, "mixtral_decode": 16, "deepseek_v3": 4, "
                  "switch_top1": 8, "scout_top1": 8, "v4_shared_top7": 4, "maverick_top1": 6}
 
 
+def test_hidden_state_beyond_4gib():
+    # H holds 140000 rows x 16384 bf16 = 4.6 GB: the out-projection reads each tile's rows from
+    # that tile's own base, since 32-bit byte offsets from the start of H end at row 131072;
+    # tokens whose rows lie past that are checked
+    cfg = W.LayerConfig("h_beyond_4gib", T=140000, d=64, N=2, k=1, d_ff=16384, dtype="bf16", ffn=W.FFN_SWIGLU,
+                        gating=W.GATE_TOPK_SOFTMAX, seed=29)
+    log(f"[{cfg.name}] T={cfg.T} d={cfg.d} N={cfg.N} k={cfg.k} d_ff={cfg.d_ff}")
+    inp = W.make_inputs(cfg, "cuda")
+    layer, y, r = run_layer(cfg, inp)
+    rn = routing_to_np(r)
+    z64, zerr, alike = check_routing(cfg, inp, rn)
+    far = np.nonzero(alike & (rn["inv"].reshape(cfg.T, cfg.k)[:, 0] >= (1 << 32) // (2 * cfg.d_ff)))[0]
+    near = np.nonzero(alike)[0]
+    rng = np.random.default_rng(cfg.seed)
+    assert far.size >= 6
+    tokens = np.unique(np.concatenate([rng.choice(far, 6, replace=False), rng.choice(near, 2, replace=False)]))
+    ref = oracle_forward(cfg, inp, tokens=tokens, z=z64)
+    check_y(cfg, f64(y)[tokens], ref["y"], label=f" sampled tokens {tokens.tolist()}:")
+    del layer, y, r, inp
+    _free()
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_layer(name):
     cfg = C[name]
