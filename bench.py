@@ -17,7 +17,6 @@ from __future__ import annotations
 import argparse
 import ctypes
 import json
-import math
 import os
 import re
 import sys

@@ -16,7 +16,7 @@ import torch
 import mixture_experts_layer_48_amd as M
 import oracle as O
 import workloads as W
-from gpu_harness import check_stats, check_y, desc_of, f64, gpu_routing_stats, log, oracle_forward, run_layer
+from gpu_harness import check_stats, check_y, f64, gpu_routing_stats, log, oracle_forward, run_layer
 
 pytestmark = pytest.mark.gpu
 
