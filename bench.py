@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixtral_prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixtral_prefill] [--only]
 
 A step is one whole layer forward (router, gating, grouping, expert FFNs,
 combine) over one resident batch of synthetic inputs.  Prints one JSON line:
@@ -10,7 +10,9 @@ kernel (the grouped gate/up projection; for decode-sized batches the bytes of
 the distinct experts it reads) from HIP events recorded around that kernel on
 the layer's stream during the timed steps, per-stage device times from a second,
 untimed pass with an event at every stage boundary, and the CPU oracle timed on
-a bounded sample of the same layer.
+a bounded sample of the same layer.  The headline is the Mixtral-shaped prefill
+layer; the default run then measures the decode batch, the DeepSeek-V3 shape and
+the skewed layer with capacity the same way, under "configs" (--only skips them).
 """
 from __future__ import annotations
 
@@ -267,12 +269,128 @@ def ep_layout_timing(M, cfg, desc, inp, routing, hip, steps: int, G: int = 8):
             "unpack_gbs": 2 * R * d * 4 / max(unpack_us, 1e-3) / 1e3}
 
 
+def measure(M, W, hip, cfg, steps: int, warmup: int, weights: str = "native", extras: bool = True):
+    """Time `steps` layer forwards of one configuration (after `warmup` untimed ones) and derive
+    its throughput, roofline fractions and per-stage device times.  Returns (result dict,
+    inputs, routing) -- the inputs stay resident for the CPU baseline."""
+    import torch
+
+    inp = W.make_inputs(cfg, "cuda")
+    desc = M.make_desc(cfg.T, cfg.d, cfg.N, cfg.k, cfg.d_ff, cfg.dtype, cfg.ffn, cfg.gating,
+                       cfg.capacity_factor, cfg.has_shared)
+    qweights = M.quantize_weights_q4(inp) if weights == "int4" else None
+    layer = M.MoELayer(desc, inp, qweights=qweights)
+    routing = layer.routing_buffers()
+    y = torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device="cuda")
+    nev = M.MOE_NUM_STAGES + 1
+
+    for _ in range(warmup):
+        layer.forward(inp["x"], y=y, out_routing=routing)
+    # Timed region: the only events recorded are the two around the dominant kernel (the
+    # in-projection, stage 3), for its live duration.
+    in_ev = [(hip.create(), hip.create()) for _ in range(steps)]
+    only_in = [[None] * 3 + [a, b] + [None] * (nev - 5) for a, b in in_ev]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer.forward(inp["x"], y=y, out_routing=routing, events=only_in[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / steps
+    ffn_in_ms = sum(hip.elapsed_ms(a, b) for a, b in in_ev) / steps
+    # Stage breakdown: a second pass with an event at every stage boundary (not timed; the
+    # events themselves add a few microseconds per call).
+    events = [[hip.create() for _ in range(nev)] for _ in range(steps)]
+    for i in range(steps):
+        layer.forward(inp["x"], y=y, out_routing=routing, events=events[i])
+    torch.cuda.synchronize()
+    stage_ms = [sum(hip.elapsed_ms(ev[s], ev[s + 1]) for ev in events) / steps
+                for s in range(M.MOE_NUM_STAGES)]
+    step_dev = sorted(hip.elapsed_ms(ev[0], ev[-1]) for ev in events)
+    step_dev_ms = sum(step_dev) / steps
+    for ev in events + [list(p) for p in in_ev]:
+        for e in ev:
+            hip.destroy(e)
+
+    counts = routing["counts"].cpu().numpy()
+    alg = algorithmic_counts(cfg, counts, weight_bytes=0.5 + 4.0 / 128 if qweights is not None else None)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ai = alg["ffn_in_flops"] / alg["ffn_in_bytes"]
+    if cfg.dtype == "f32":
+        roof = {"bound": "alu", "achieved": alg["ffn_in_flops"] / (ffn_in_ms * 1e-3) / 1e12,
+                "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
+    elif ai >= ridge:
+        roof = {"bound": "mfma", "achieved": alg["ffn_in_flops"] / (ffn_in_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": alg["ffn_in_bytes"] / (ffn_in_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_from_profile(cfg.name) if qweights is None else None
+    roof["kernel"] = ("ffn_in (grouped gate/up projection)" if qweights is None
+                      else "ffn_in (gate/up projection, int4 weight stream)")
+    roof["ms_per_launch"] = ffn_in_ms
+    res = {
+        "workload": cfg.name,
+        "ms_per_step": ms_per_step,
+        "tokens_per_s": cfg.T * steps / (t1 - t0),
+        "tflops": alg["flops"] / (ms_per_step * 1e-3) / 1e12,
+        "mfma_frac": alg["flops"] / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "gbs_distinct_experts": alg["bytes"] / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac": alg["bytes"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "experts_touched": alg["touched"], "device_ms_per_step": step_dev_ms,
+        "device_ms_median": statistics.median(step_dev), "device_ms_min": step_dev[0],
+        # the time the binding roofline allows, max(flops / MFMA peak, bytes / HBM peak), over the
+        # measured time
+        "roofline_time_frac": max(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12),
+                                  alg["bytes"] / (PEAK_HBM_GBS * 1e9)) / (ms_per_step * 1e-3),
+        "stages_ms": dict(zip(M.STAGE_NAMES, stage_ms)),
+        "roofline": roof,
+        "config": {"T": cfg.T, "d": cfg.d, "N": cfg.N, "k": cfg.k, "d_ff": cfg.d_ff, "ffn": cfg.ffn,
+                   "gating": cfg.gating, "capacity_factor": cfg.capacity_factor,
+                   "shared_expert": cfg.has_shared, "expert_weights": weights},
+    }
+    if extras:
+        # Routing statistics of the same routing (outside the layer step): device time per call
+        # between two events around `steps` back-to-back calls.
+        st_out = None
+        ev_a, ev_b = hip.create(), hip.create()
+        layer.routing_stats(routing)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream().cuda_stream
+        hip.record(ev_a, stream)
+        for _ in range(steps):
+            st_out = layer.routing_stats(routing)
+        hip.record(ev_b, stream)
+        torch.cuda.synchronize()
+        stats_us = hip.elapsed_ms(ev_a, ev_b) * 1e3 / steps
+        hip.destroy(ev_a)
+        hip.destroy(ev_b)
+        st_vals = st_out["stats"].cpu().numpy().tolist()
+        # algorithmic bytes: logits, indices and counts read once, the statistics written
+        st_bytes = cfg.T * cfg.N * 4 + cfg.T * cfg.k * 4 + cfg.N * 4 + M.MOE_NUM_STATS * 8 + 3 * 4
+        res["routing_stats"] = {"us_per_call": stats_us, "gbs": st_bytes / (stats_us * 1e-6) / 1e9,
+                                "values": dict(zip(M.STAT_NAMES, st_vals)),
+                                "top3": st_out["top3"].cpu().numpy().tolist()}
+        res["ep_layout"] = ep_layout_timing(M, cfg, desc, inp, routing, hip, steps)
+    del layer, y, qweights
+    return res, inp, routing
+
+
+# The other layer shapes of the metric, measured after the headline one in the default run: the
+# decode batch (scored on HBM bandwidth of the distinct experts it reads), the DeepSeek-V3 shape and
+# the skewed layer with capacity (scored on MFMA and on HBM).
+SECONDARY = ("mixtral_decode", "deepseek_v3", "skewed_capacity")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_prefill")
+    ap.add_argument("--only", action="store_true",
+                    help="measure --config alone (without the other layer shapes of the default run)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weights", choices=("native", "int4"), default="native",
@@ -291,7 +409,6 @@ def main(argv=None) -> int:
               f"supported (run with --gpus 1)", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
     import mixture_experts_layer_48_amd as M
     import workloads as W
@@ -309,120 +426,48 @@ def main(argv=None) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    inp = W.make_inputs(cfg, "cuda")
-    desc = M.make_desc(cfg.T, cfg.d, cfg.N, cfg.k, cfg.d_ff, cfg.dtype, cfg.ffn, cfg.gating,
-                       cfg.capacity_factor, cfg.has_shared)
-    qweights = M.quantize_weights_q4(inp) if args.weights == "int4" else None
-    layer = M.MoELayer(desc, inp, qweights=qweights)
-    routing = layer.routing_buffers()
-    y = torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device="cuda")
     hip = HipEvents()
-    nev = M.MOE_NUM_STAGES + 1
-
-    for _ in range(args.warmup):
-        layer.forward(inp["x"], y=y, out_routing=routing)
-    # Timed region: the only events recorded are the two around the dominant kernel (the
-    # in-projection, stage 3), for its live duration.
-    in_ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
-    only_in = [[None] * 3 + [a, b] + [None] * (nev - 5) for a, b in in_ev]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        layer.forward(inp["x"], y=y, out_routing=routing, events=only_in[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1000.0 / args.steps
-    ffn_in_ms = sum(hip.elapsed_ms(a, b) for a, b in in_ev) / args.steps
-    # Stage breakdown: a second pass with an event at every stage boundary (not timed; the
-    # events themselves add a few microseconds per call).
-    events = [[hip.create() for _ in range(nev)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        layer.forward(inp["x"], y=y, out_routing=routing, events=events[i])
-    torch.cuda.synchronize()
-    stage_ms = [sum(hip.elapsed_ms(ev[s], ev[s + 1]) for ev in events) / args.steps
-                for s in range(M.MOE_NUM_STAGES)]
-    step_dev = sorted(hip.elapsed_ms(ev[0], ev[-1]) for ev in events)
-    step_dev_ms = sum(step_dev) / args.steps
-    # Routing statistics of the same routing (outside the layer step): device time per call
-    # between two events around `steps` back-to-back calls.
-    st_out = None
-    ev_a, ev_b = hip.create(), hip.create()
-    layer.routing_stats(routing)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream().cuda_stream
-    hip.record(ev_a, stream)
-    for _ in range(args.steps):
-        st_out = layer.routing_stats(routing)
-    hip.record(ev_b, stream)
-    torch.cuda.synchronize()
-    stats_us = hip.elapsed_ms(ev_a, ev_b) * 1e3 / args.steps
-    events.append([ev_a, ev_b])
-    for ev in events + [list(p) for p in in_ev]:
-        for e in ev:
-            hip.destroy(e)
-    ep_layout = ep_layout_timing(M, cfg, desc, inp, routing, hip, args.steps)
-    st_vals = st_out["stats"].cpu().numpy().tolist()
-    # algorithmic bytes: logits, indices and counts read once, the statistics written
-    st_bytes = cfg.T * cfg.N * 4 + cfg.T * cfg.k * 4 + cfg.N * 4 + M.MOE_NUM_STATS * 8 + 3 * 4
-    routing_stats = {"us_per_call": stats_us, "gbs": st_bytes / (stats_us * 1e-6) / 1e9,
-                     "values": dict(zip(M.STAT_NAMES, st_vals)),
-                     "top3": st_out["top3"].cpu().numpy().tolist()}
-
-    counts = routing["counts"].cpu().numpy()
-    alg = algorithmic_counts(cfg, counts, weight_bytes=0.5 + 4.0 / 128 if qweights is not None else None)
-    tokens_per_s = cfg.T * args.steps / (t1 - t0)
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    ai = alg["ffn_in_flops"] / alg["ffn_in_bytes"]
-    if cfg.dtype == "f32":
-        roof = {"bound": "alu", "achieved": alg["ffn_in_flops"] / (ffn_in_ms * 1e-3) / 1e12,
-                "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
-    elif ai >= ridge:
-        roof = {"bound": "mfma", "achieved": alg["ffn_in_flops"] / (ffn_in_ms * 1e-3) / 1e12,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": alg["ffn_in_bytes"] / (ffn_in_ms * 1e-3) / 1e9,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_from_profile(cfg.name) if qweights is None else None
-    roof["kernel"] = ("ffn_in (grouped gate/up projection)" if qweights is None
-                      else "ffn_in (gate/up projection, int4 weight stream)")
+    res, inp, _ = measure(M, W, hip, cfg, args.steps, args.warmup, args.weights)
+    print(f"# {cfg.name}: {res['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": res["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype if qweights is None else "bf16 activations, int4 expert weights",
+        "dtype": cfg.dtype if args.weights == "native" else "bf16 activations, int4 expert weights",
         "data": "synthetic (seeded Gaussian inputs and weights of the layer's shapes)",
-        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "N": cfg.N, "k": cfg.k, "d_ff": cfg.d_ff,
-                   "ffn": cfg.ffn, "gating": cfg.gating, "capacity_factor": cfg.capacity_factor,
-                   "shared_expert": cfg.has_shared, "expert_weights": args.weights},
-        "layer": {"tflops": alg["flops"] / (ms_per_step * 1e-3) / 1e12,
-                  "mfma_frac": alg["flops"] / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                  "gbs_distinct_experts": alg["bytes"] / (ms_per_step * 1e-3) / 1e9,
-                  "hbm_frac": alg["bytes"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                  "experts_touched": alg["touched"], "device_ms_per_step": step_dev_ms,
-                  "device_ms_median": statistics.median(step_dev), "device_ms_min": step_dev[0],
-                  # the time the binding roofline allows, max(flops / MFMA peak, bytes / HBM peak),
-                  # over the measured time
-                  "roofline_time_frac": max(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12),
-                                            alg["bytes"] / (PEAK_HBM_GBS * 1e9)) / (ms_per_step * 1e-3)},
-        "stages_ms": dict(zip(M.STAGE_NAMES, stage_ms)),
-        "routing_stats": routing_stats,
-        "ep_layout": ep_layout,
-        "roofline": roof,
+        "config": dict(workload=cfg.name, **res["config"]),
+        "layer": {k: res[k] for k in ("tflops", "mfma_frac", "gbs_distinct_experts", "hbm_frac",
+                                      "experts_touched", "device_ms_per_step", "device_ms_median",
+                                      "device_ms_min", "roofline_time_frac")},
+        "stages_ms": res["stages_ms"],
+        "routing_stats": res["routing_stats"],
+        "ep_layout": res["ep_layout"],
+        "roofline": res["roofline"],
         "cpu_baseline": None,
+        "configs": {},
     }
     if not args.no_cpu_baseline:
         # samples sized for roughly 10-30 s of oracle work on a 16-core host
         default_sample = {"tiny_fp32": 128, "mixtral_prefill": 4096, "mixtral_decode": 16,
                           "deepseek_v3": 256, "skewed_capacity": 2048}.get(cfg.name, 64)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens or default_sample)
+    del inp
+    torch.cuda.empty_cache()
+    if not args.only and args.weights == "native" and cfg.name == "mixtral_prefill":
+        for name in SECONDARY:
+            r2, inp2, _ = measure(M, W, hip, W.CONFIGS[name], args.steps, args.warmup, extras=False)
+            print(f"# {name}: {r2['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+            r2.pop("workload")
+            out["configs"][name] = r2
+            del inp2
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
     return 0
 

@@ -62,6 +62,9 @@ moe_status check_desc(const moe_layer_desc* d) {
     // the grouped GEMM gathers x rows through 32-bit byte offsets from one base
     if (d->dtype == MOE_BF16 && (long long)d->T * d->d * 2 >= (1LL << 32))
         return fail(MOE_ERR_UNSUPPORTED, "bf16 x larger than 4 GiB (T*d*2 >= 2^32)");
+    // and reads one expert's weight matrix through 32-bit byte offsets from the matrix's start
+    if (d->dtype == MOE_BF16 && (long long)d->d * d->d_ff * 2 >= (1LL << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "bf16 expert weight matrix of 4 GiB or more (d*d_ff*2 >= 2^32)");
     return MOE_OK;
 }
 

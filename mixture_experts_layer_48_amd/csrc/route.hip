@@ -7,6 +7,7 @@
 // "大模型MoE混合专家架构原理与DeepSeek-V4工程实践解析", section MoE核心机制).
 // Capacity: a full expert passes the token on to its next-best expert (page "MoE稀疏激活原理与
 // 工程实践", section 2.2).
+#include <cstdlib>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -290,14 +291,16 @@ __global__ __launch_bounds__(64) void rank_sort_kernel(const float* __restrict__
 // window keeps a chunk at one token per thread.  "Room at chunk start" is a byte table in LDS
 // and "already held" is in registers; a scan takes 16 ranks at a time, so a token steps over
 // full experts cheaply.  Proposal
-// counts are per wave, stamped with the round number, so no round has to clear them.
+// counts are per wave, stamped with the round number, so no round has to clear them; after
+// round_limit rounds (at most 0xFFFF, the stamp's width) the counts are cleared and the stamps
+// start again at 1, at the top of a round, when no earlier round's count is read any more.
 #define CAP_THREADS 1024
 #define CAP_WIN 4                   // 16-byte pieces (16 ranks each) in a token's window
 
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void capacity_kernel(
     const uint8_t* __restrict__ ranked, uint8_t* __restrict__ rpos, int T, int N, int NP, int CT, int k,
-    int C, int32_t* __restrict__ idx) {
+    int C, uint32_t round_limit, int32_t* __restrict__ idx) {
     constexpr int CAP_THREADS_ = THREADS;
     constexpr int CAP_WAVES_ = THREADS / 64;
     constexpr int WW = 4 * CAP_WIN;                     // window words
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
     const int NQ = NP >> 2;               // words per ranked row (multiple of 4)
     for (int e = tid; e < MOE_MAX_EXPERTS; e += CAP_THREADS_) fill[e] = 0;
     for (int i = tid; i < CAP_WAVES_ * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&cnt[0][0])[i] = 0u;
-    uint32_t round = 0;                   // stamps of cnt; never reused without clearing
+    uint32_t round = 0;                   // stamp of the current round's counts, 1 .. round_limit
 
     // next chunk's state of this thread's token, fetched during the current chunk: the window
     // of its ranked row, the first four experts it already holds and the rank after its
@@ -370,6 +373,13 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
             int q = start >> 2, bpos = start & 3, choice = -1;
             bool choose = active;
             while (true) {
+                // round is uniform over the block (every thread runs every round), and the
+                // barrier that ended the previous round follows its last read of cnt
+                if (round >= round_limit) {
+                    for (int i = tid; i < CAP_WAVES_ * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&cnt[0][0])[i] = 0u;
+                    round = 0;
+                    __syncthreads();                      // cleared before any new stamp is written
+                }
                 ++round;
                 if (choose) {                             // next candidate from (q, bpos) on
                     choice = -1;
@@ -466,11 +476,6 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                 }
                 fill[tid] += s;
             }
-            if (round >= 0xFFF0) {                        // keep stamps unique: clear and restart
-                __syncthreads();
-                for (int i = tid; i < CAP_WAVES_ * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&cnt[0][0])[i] = 0u;
-                round = 0;
-            }
             __syncthreads();
         }
     }
@@ -552,6 +557,16 @@ hipError_t launch_topk_gate(const float* z, int T, int N, int k, int gating, int
     return hipGetLastError();
 }
 
+// Rounds between two clears of the capacity kernel's proposal counts: 0xFFFF (the stamp's
+// width), or the value of MOE_CAPACITY_ROUND_LIMIT (1 .. 0xFFFF), a testing hook that makes the
+// clears frequent so that their path is exercised; the routing does not depend on it.
+static uint32_t capacity_round_limit() {
+    const char* v = getenv("MOE_CAPACITY_ROUND_LIMIT");
+    if (!v || !*v) return 0xFFFFu;
+    const long n = strtol(v, nullptr, 10);
+    return n < 1 ? 1u : n > 0xFFFF ? 0xFFFFu : (uint32_t)n;
+}
+
 int capacity_ranked_stride(int N) { return (N + 15) & ~15; }
 size_t capacity_workspace_bytes(int T, int N) { return (size_t)T * capacity_ranked_stride(N) + (size_t)T; }
 
@@ -566,7 +581,7 @@ hipError_t launch_capacity(const float* z, uint8_t* ranked, int T, int N, int k,
     const int CT = CAP_THREADS;
     auto kern = capacity_kernel<CAP_THREADS>;
     hipLaunchKernelGGL(kern, dim3(1), dim3(CAP_THREADS), 0, s, ranked, ranked + (size_t)T * NP, T, N, NP, CT,
-                       k, C, idx);
+                       k, C, capacity_round_limit(), idx);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(slot_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, z, idx, T, N, k, gating, w);

@@ -62,6 +62,14 @@ def test_x_size_limit_applies_to_bf16_only():
     assert M.moe_workspace_size(_desc(T=1 << 19, d=4096, dtype="f32")) > 0
 
 
+def test_expert_matrix_size_limit_applies_to_bf16_only():
+    # one expert's weight matrix is read through 32-bit byte offsets: d * d_ff * 2 < 2^32 on bf16
+    assert M.moe_workspace_size(_desc(T=16, d=65536, d_ff=32768 - 64)) > 0
+    assert M.moe_workspace_size(_desc(T=16, d=65536, d_ff=32768)) == 0
+    assert M.moe_workspace_size(_desc(T=16, d=32768, d_ff=65536)) == 0
+    assert M.moe_workspace_size(_desc(T=16, d=65536, d_ff=32768, dtype="f32")) > 0
+
+
 FAKE = 0x1000   # never dereferenced: every call below fails validation on the host
 
 
@@ -79,6 +87,7 @@ FAKE = 0x1000   # never dereferenced: every call below fails validation on the h
     (dict(d=100), M.MOE_ERR_UNSUPPORTED),
     (dict(d_ff=200), M.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 19, d=4096), M.MOE_ERR_UNSUPPORTED),     # bf16 x of exactly 4 GiB
+    (dict(d=65536, d_ff=32768), M.MOE_ERR_UNSUPPORTED),   # bf16 expert matrix of exactly 4 GiB
 ])
 def test_descriptor_errors(lib, kw, status):
     desc = _desc(**kw)

@@ -5,7 +5,7 @@ The quantisation kernel must give the oracle's codes and scales bit for bit
 oracle's forward with the weights the codes stand for (scale * q, float64),
 to the bf16 layers' bar.  Small layers use a selection router (exact logits,
 so every token is routed alike and compared); the full Mixtral-shaped decode
-layer is checked on sampled tokens, as the bf16 full-size layers are."""
+layer is checked on every token, as the bf16 full-size layers are."""
 import numpy as np
 import pytest
 import torch
@@ -62,17 +62,15 @@ def test_quantize_ties_and_grid():
 
 
 class QExpertView:
-    """Index -> one expert's dequantised weights (the oracle quantises the bf16 weights itself)."""
+    """Index -> one expert's dequantised weights (the oracle quantises the bf16 weights itself),
+    computed on each access and not kept."""
 
     def __init__(self, t):
-        self.t, self.cache = t, {}
+        self.t = t
 
     def __getitem__(self, e):
-        e = int(e)
-        if e not in self.cache:
-            q, sc = O.quantize_q4(self.t[e].float().cpu().numpy())
-            self.cache[e] = O.dequantize_q4(q, sc)
-        return self.cache[e]
+        q, sc = O.quantize_q4(self.t[int(e)].float().cpu().numpy())
+        return O.dequantize_q4(q, sc)
 
 
 def _oracle_q4_forward(cfg, inp, tokens=None, z=None):
@@ -143,8 +141,5 @@ def test_q4_mixtral_decode_full_size():
     codes = qw["w_gate_codes"][0].cpu().numpy().view(np.uint32)
     oc, osc = _oracle_codes(inp["w_gate"][0].float().cpu().numpy())
     assert np.array_equal(codes, oc) and np.array_equal(qw["w_gate_scales"][0].cpu().numpy(), osc.T)
-    rng = np.random.default_rng(cfg.seed)
-    pool = np.nonzero(alike)[0]
-    tokens = np.sort(rng.choice(pool, size=min(4, pool.size), replace=False))
-    ref = _oracle_q4_forward(cfg, inp, tokens=tokens, z=z64)
-    check_y(cfg, f64(y)[tokens], ref["y"], label=f" sampled tokens {tokens.tolist()}:")
+    ref = _oracle_q4_forward(cfg, inp, z=z64)
+    check_y(cfg, f64(y)[alike], ref["y"][alike], label=f" all {int(alike.sum())} of {cfg.T} tokens routed alike:")
