@@ -195,6 +195,27 @@ moe_status moe_layer_forward_timed(const moe_layer_desc *desc, const moe_weights
                                    void *ws, size_t ws_bytes, moe_stream_t stream,
                                    void *const *events);
 
+/* Bytes of the built-in workspace of moe_layer_forward_noalloc (one array per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_layer_forward without a caller workspace and without any allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The workspace is a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) in the library, one per GPU, created with the library's
+ * code object and held until the process ends; its device address is looked up once per device
+ * (hipGetSymbolAddress, on the first call made with that device current).  The caller still
+ * passes x, y and the optional routing outputs, as for moe_layer_forward; `stream` must belong
+ * to the current device.
+ * Errors: MOE_ERR_UNSUPPORTED (before anything is enqueued) when moe_workspace_size(desc)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES -- decode-sized batches fit, e.g. T <= 256 tokens on a
+ * Mixtral-8x7B-shaped layer -- plus every error of moe_layer_forward.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents (nothing
+ * in it needs to start at zero): calls that overlap on one GPU, on different streams or from
+ * different threads, race and give undefined results; serialise them. */
+moe_status moe_layer_forward_noalloc(const moe_layer_desc *desc, const moe_weights *weights,
+                                     const void *x, void *y, const moe_routing *routing,
+                                     moe_stream_t stream);
+
 /* Number of values moe_routing_stats() writes to `stats`, in this order:
  *   0 entropy_bits        -sum_i f_i log2 f_i over experts with f_i > 0, f_i = counts[i] / sum(counts)
  *   1 entropy_ideal_bits  log2 N (every expert with the same share)

@@ -23,6 +23,7 @@ MOE_NUM_STAGES = 6
 STAGE_NAMES = ("route", "capacity", "permute", "ffn_in", "ffn_out", "combine")
 MOE_NUM_STATS = 8
 MOE_EP_MAX_RANKS = 64
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 STAT_NAMES = ("entropy_bits", "entropy_ideal_bits", "top3_share", "max_share", "cv", "balance_loss",
               "reroute_rate", "experts_touched")
 
@@ -93,6 +94,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.POINTER(moe_routing), vp, sz, vp]
     lib.moe_layer_forward_timed.argtypes = [pdesc, ctypes.POINTER(moe_weights), vp, vp,
                                             ctypes.POINTER(moe_routing), vp, sz, vp, ctypes.POINTER(vp)]
+    lib.moe_layer_forward_noalloc.argtypes = [pdesc, ctypes.POINTER(moe_weights), vp, vp,
+                                              ctypes.POINTER(moe_routing), vp]
     lib.moe_routing_stats.argtypes = [pdesc, vp, vp, vp, ctypes.c_double, vp, vp, vp, vp, sz, vp]
     pi32 = ctypes.POINTER(ctypes.c_int32)
     pq4 = ctypes.POINTER(moe_weights_q4)
@@ -105,7 +108,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                           ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.moe_ep_unpack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-              "moe_layer_forward_timed", "moe_routing_stats", "moe_ep_dispatch", "moe_ep_receive_layout",
+              "moe_layer_forward_timed", "moe_layer_forward_noalloc", "moe_routing_stats", "moe_ep_dispatch", "moe_ep_receive_layout",
               "moe_ep_unpack", "moe_quantize_q4", "moe_expert_ffn_q4", "moe_layer_forward_q4"):
         getattr(lib, f).restype = i32
     lib.moe_status_str.argtypes = [i32]
@@ -196,6 +199,16 @@ def moe_layer_forward(desc, weights: Dict, x, y, routing: Optional[Dict] = None,
         st = lib.moe_layer_forward_timed(ctypes.byref(desc), ctypes.byref(wt), _ptr(x), _ptr(y), ctypes.byref(r),
                                          _ptr(ws), ws_bytes, _stream(stream), arr)
         _check(st, "moe_layer_forward_timed")
+
+
+def moe_layer_forward_noalloc(desc, weights: Dict, x, y, routing: Optional[Dict] = None, stream=None) -> None:
+    """The whole layer on the library's built-in per-GPU workspace (MOE_NOALLOC_SCRATCH_BYTES):
+    no workspace argument and no allocation."""
+    wt = _weights(weights)
+    r = moe_routing(*(_ptr((routing or {}).get(n)) for n in
+                      ("logits", "idx", "w", "counts", "offsets", "perm", "inv")))
+    _check(load_library().moe_layer_forward_noalloc(ctypes.byref(desc), ctypes.byref(wt), _ptr(x), _ptr(y),
+                                                    ctypes.byref(r), _stream(stream)), "moe_layer_forward_noalloc")
 
 
 def moe_routing_stats(desc, logits, idx, counts, stats, top3, ws, alpha: float = 0.01, prob_mean=None,

@@ -7,10 +7,17 @@
 #include <cmath>
 #include <cstdio>
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
 #include "moe_kernels.h"
+
+// Workspace of moe_layer_forward_noalloc: one array of MOE_NOALLOC_SCRATCH_BYTES per GPU the
+// library runs on, created with the code object and held until the process ends.  Host code
+// never uses this name as an address (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -247,6 +254,8 @@ moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int
     return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 
+}  // extern "C"
+
 namespace {
 // The whole layer; q4 != nullptr selects the int4 expert weights (the FFN weight pointers of
 // `weights` are then ignored).
@@ -317,6 +326,8 @@ moe_status check_q4(const moe_layer_desc& d, const moe_weights_q4* w, bool need_
 }
 }  // namespace
 
+extern "C" {
+
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
                                    void* y, const moe_routing* routing, void* ws, size_t ws_bytes,
                                    moe_stream_t stream, void* const* events) {
@@ -383,6 +394,67 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_weights* weig
     return moe_layer_forward_timed(desc, weights, x, y, routing, ws, ws_bytes, stream, nullptr);
 }
 
+}  // extern "C"
+
+namespace {
+#define MOE_NOALLOC_MAX_DEVICES 64
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MOE_NOALLOC_MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array, looked up with that device current on
+// its first use and kept per device (each GPU holds its own copy of the array).  `stream` must
+// belong to the current device.
+moe_status noalloc_scratch(hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= MOE_NOALLOC_MAX_DEVICES)
+        return fail(MOE_ERR_UNSUPPORTED, "device index beyond " + std::to_string(MOE_NOALLOC_MAX_DEVICES));
+    if (stream) {
+        int sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+        if (sdev != dev)
+            return fail(MOE_ERR_INVALID_ARG, "stream belongs to device " + std::to_string(sdev) +
+                                                 ", the current device is " + std::to_string(dev));
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
+                                     void* y, const moe_routing* routing, moe_stream_t stream) {
+    g_err.clear();
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    st = check_weights(*desc, weights, true, true);
+    if (st != MOE_OK) return st;
+    const size_t need = layout_of(*desc).total;
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_layer_forward_noalloc: this layer needs " + std::to_string(need) +
+                                             " bytes of workspace; the built-in scratch holds " +
+                                             std::to_string((size_t)MOE_NOALLOC_SCRATCH_BYTES) +
+                                             " (use moe_layer_forward with a workspace)");
+    if (desc->T == 0) return MOE_OK;
+    if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x and y are required");
+    void* ws = nullptr;
+    if ((st = noalloc_scratch((hipStream_t)stream, &ws)) != MOE_OK) return st;
+    // nothing in the forward's workspace has to start at zero: every piece is written before it
+    // is read within the call, so the previous call's contents do no harm
+    return forward_impl(*desc, *weights, nullptr, x, y, routing, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES,
+                        (hipStream_t)stream, nullptr);
+}
+
 moe_status moe_routing_stats(const moe_layer_desc* desc, const float* logits, const int32_t* idx,
                              const int32_t* counts, double alpha, double* stats, int32_t* top3, double* prob_mean,
                              void* ws, size_t ws_bytes, moe_stream_t stream) {
@@ -402,6 +474,8 @@ moe_status moe_routing_stats(const moe_layer_desc* desc, const float* logits, co
     return e == hipSuccess ? MOE_OK : hip_fail(e, "routing statistics launch");
 }
 
+}  // extern "C"
+
 namespace {
 moe_status check_owner(const int32_t* owner, int N, int G) {
     if (G < 1 || G > MOE_EP_MAX_RANKS) return fail(MOE_ERR_INVALID_ARG, "G must satisfy 1 <= G <= 64");
@@ -412,6 +486,8 @@ moe_status check_owner(const int32_t* owner, int N, int G) {
     return MOE_OK;
 }
 }  // namespace
+
+extern "C" {
 
 moe_status moe_ep_dispatch(const moe_layer_desc* desc, const int32_t* idx, const int32_t* owner, int32_t G,
                            int32_t* counts, int32_t* expert_offsets, int32_t* send_counts, int32_t* send_offsets,
