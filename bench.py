@@ -184,40 +184,46 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str
     return "\n".join(lines) + "\n"
 
 
-def cpu_baseline(cfg, inp, sample_tokens: int):
-    """The float64 CPU oracle, as it stands, on the first `sample_tokens` tokens of the same layer
-    (same weights; the oracle reads each touched expert's weights once, converted to float64)."""
-    import numpy as np
-    import oracle as O
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, sample_tokens: int, one_core_tokens: int):
+    """The plain C++ float64 oracle (oracle/moe_oracle.cpp), as it stands, on the same layer and
+    weights (host copies of the device tensors, bf16 read in place): routing of every token, then
+    the expert FFNs and combine of the first `sample_tokens` tokens on all host cores this process
+    may use, and of the first `one_core_tokens` on one core.  tokens/s counts the sampled tokens."""
+    import oracle.cpp as OC
+    host = {k: (None if v is None else v.cpu()) for k, v in inp.items()}
+    shared = (host["sh_gate"], host["sh_up"], host["sh_down"]) if cfg.has_shared else None
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+
+    def run(threads, S):
+        OC.set_threads(threads)
+        t0 = time.perf_counter()
+        OC.forward(host["x"], host["w_router"], host["w_up"], host["w_down"], cfg.k, cfg.ffn, cfg.gating,
+                   w_gate=host["w_gate"], logit_bias=host["logit_bias"], capacity_factor=cfg.capacity_factor,
+                   shared=shared, tokens=list(range(S)))
+        return time.perf_counter() - t0
+
     S = min(sample_tokens, cfg.T)
-
-    class View:
-        def __init__(self, t):
-            self.t = t
-
-        def __getitem__(self, e):
-            return self.t[int(e)].float().cpu().numpy().astype(np.float64)
-
-    def f64(t):
-        return None if t is None else t.float().cpu().numpy().astype(np.float64)
-
-    t0 = time.perf_counter()
-    shared = (f64(inp["sh_gate"]), f64(inp["sh_up"]), f64(inp["sh_down"])) if cfg.has_shared else None
-    O.forward(f64(inp["x"][:S]), f64(inp["w_router"]), View(inp["w_up"]), View(inp["w_down"]), cfg.k,
-              O.SWIGLU if cfg.ffn == "swiglu" else O.RELU2,
-              O.TOPK_SOFTMAX if cfg.gating == "topk_softmax" else O.SOFTMAX_TOPK,
-              w_gate=View(inp["w_gate"]) if inp["w_gate"] is not None else None,
-              logit_bias=None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy(),
-              capacity_factor=cfg.capacity_factor, shared=shared)
-    dt = time.perf_counter() - t0
-    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"layer forward on the first {S} of {cfg.T} tokens (same layer and weights), float64, "
-                      f"{dt:.1f} s including the float64 conversion of each touched expert's weights"}
+    S1 = min(one_core_tokens, cfg.T)
+    dt = run(cores, S)
+    dt1 = run(1, S1)
+    OC.set_threads(cores)
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"C++ float64 oracle: routing of all {cfg.T} tokens, expert FFNs and combine of the first "
+                      f"{S} tokens of the same layer and weights on {cores} threads, {dt:.1f} s",
+            "one_core": {"value": S1 / dt1, "unit": "tokens/s", "cores": 1,
+                         "sample": f"first {S1} tokens on one thread, {dt1:.1f} s"},
+            "cpu_model": cpu_model(), "nproc": os.cpu_count()}
 
 
 def ep_layout_timing(M, cfg, desc, inp, routing, hip, steps: int, G: int = 8):
@@ -454,10 +460,11 @@ def main(argv=None) -> int:
         "configs": {},
     }
     if not args.no_cpu_baseline:
-        # samples sized for roughly 10-30 s of oracle work on a 16-core host
-        default_sample = {"tiny_fp32": 128, "mixtral_prefill": 4096, "mixtral_decode": 16,
+        # samples sized for roughly 10-20 s of oracle work each, on 16 host cores and on one
+        default_sample = {"tiny_fp32": 128, "mixtral_prefill": 256, "mixtral_decode": 16,
                           "deepseek_v3": 256, "skewed_capacity": 2048}.get(cfg.name, 64)
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens or default_sample)
+        S = args.cpu_sample_tokens or default_sample
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, S, max(1, S // 16))
     del inp
     torch.cuda.empty_cache()
     if not args.only and args.weights == "native" and cfg.name == "mixtral_prefill":

@@ -28,9 +28,10 @@
  *
  * Conventions
  *  - All tensors are row-major and contiguous, on the device unless stated otherwise.
- *  - Weights are stored output-major, one row per output feature (a linear layer's weight):
- *      w_router [N, d]; w_gate, w_up [N, d_ff, d]; w_down [N, d, d_ff];
- *      shared expert: sh_gate, sh_up [d_ff, d], sh_down [d, d_ff].
+ *  - Weights are in the x W orientation of the pages' toy ([P2] 代码: router_W [d, N],
+ *    x @ experts_W[e]), row-major with the output index fastest:
+ *      w_router [d, N]; w_gate, w_up [N, d, d_ff]; w_down [N, d_ff, d];
+ *      shared expert: sh_gate, sh_up [d, d_ff], sh_down [d_ff, d].
  *    For MOE_FFN_RELU2, w_up holds W1 and w_down holds W2 (y = relu(x W1) W2); w_gate unused.
  *  - Activations and weights share one dtype (MOE_F32 or MOE_BF16).  Logits, gate weights
  *    and every accumulation are fp32; the router accumulates fp32 partial sums of 256
@@ -67,8 +68,8 @@
  *    counts.  In y_perm its output for token t sits at row T*k + t.
  *
  * Limits: 1 <= k <= N <= 256; T >= 0 (T = 0 is a no-op); d, d_ff >= 1.  For MOE_BF16:
- *   d % 64 == 0 and d_ff % 64 == 0, and x at most 4 GiB: T * d * 2 < 2^32 bytes (else
- *   MOE_ERR_UNSUPPORTED).  MOE_F32 has no divisibility requirement.  T * k must fit in int32
+ *   d % 64 == 0 and d_ff % 64 == 0, x below 4 GiB (T * d * 2 < 2^32 bytes) and one expert
+ *   matrix below 4 GiB (d * d_ff * 2 < 2^32 bytes), else MOE_ERR_UNSUPPORTED.  MOE_F32 has no divisibility requirement.  T * k must fit in int32
  *   with T*k + T + 1 < 2^31.
  */
 #ifndef MOE_H_
@@ -112,14 +113,14 @@ typedef struct {
 
 /* Device pointers to the layer's weights (layouts in the header comment). */
 typedef struct {
-    const void *w_router;      /* [N, d] */
+    const void *w_router;      /* [d, N] */
     const float *logit_bias;   /* [N] fp32, or NULL */
-    const void *w_gate;        /* [N, d_ff, d]; NULL for MOE_FFN_RELU2 */
-    const void *w_up;          /* [N, d_ff, d] (W1 for RELU2) */
-    const void *w_down;        /* [N, d, d_ff] (W2 for RELU2) */
-    const void *sh_gate;       /* [d_ff, d] or NULL (required with has_shared and SWIGLU) */
-    const void *sh_up;         /* [d_ff, d] or NULL (required with has_shared) */
-    const void *sh_down;       /* [d, d_ff] or NULL (required with has_shared) */
+    const void *w_gate;        /* [N, d, d_ff]; NULL for MOE_FFN_RELU2 */
+    const void *w_up;          /* [N, d, d_ff] (W1 for RELU2) */
+    const void *w_down;        /* [N, d_ff, d] (W2 for RELU2) */
+    const void *sh_gate;       /* [d, d_ff] or NULL (required with has_shared and SWIGLU) */
+    const void *sh_up;         /* [d, d_ff] or NULL (required with has_shared) */
+    const void *sh_down;       /* [d_ff, d] or NULL (required with has_shared) */
 } moe_weights;
 
 /* Optional routing outputs of moe_layer_forward (device pointers; any may be NULL). */
@@ -143,7 +144,7 @@ size_t moe_workspace_size(const moe_layer_desc *desc);
 
 /* Steps 1-3 [P1 步驟二, P2 深入原理, P3 MoE核心机制, P5 2.2]: router GEMM, ranking, gating
  * and (if capacity_factor > 0) capacity routing.
- *   x [T, d] (layer dtype); w_router [N, d]; logit_bias [N] fp32 or NULL.
+ *   x [T, d] (layer dtype); w_router [d, N]; logit_bias [N] fp32 or NULL.
  *   logits [T, N] fp32 output or NULL; idx [T, k] int32 and w [T, k] fp32 outputs (required).
  *   ws/ws_bytes: workspace of at least moe_workspace_size(desc) bytes. */
 moe_status moe_route(const moe_layer_desc *desc, const void *x, const void *w_router,
@@ -247,12 +248,13 @@ moe_status moe_routing_stats(const moe_layer_desc *desc, const float *logits, co
 
 /* ---- Int4 expert weights for weight-streaming (decode) layers [P3 DeepSeek-V4的MoE架构工程细节:
  * GPTQ/AWQ INT4 expert weights at a quarter of the memory; the pages give no format].  Format:
- * per weight row and group of 128 consecutive inputs, scale = amax / 7 (fp32), q =
- * clamp(rint(w / scale), -8, 7) (fp32 division, ties to even; all-zero group: scale 0, q 0); the
- * weight stands for scale * q.  Codes q + 8, four bits each, eight per uint32: within row r and
- * group g, word 4a + s (a, s in 0..3) holds inputs k = 128g + 32s + 8a + i (i = 0..7), input i
- * at bit 4 (i / 2) + 16 (i % 2).  A stack of n matrices [rows, K]: codes [n, rows, K / 8] uint32,
- * scales [n, K / 128, rows] fp32 (device). */
+ * per output r (a column of a [K, rows] weight matrix) and group of 128 consecutive inputs,
+ * scale = amax / 7 (fp32), q = clamp(rint(w / scale), -8, 7) (fp32 division, ties to even;
+ * all-zero group: scale 0, q 0); the weight stands for scale * q.  Codes q + 8, four bits each,
+ * eight per uint32, one row of words per output: within output r and group g, word 4a + s (a, s
+ * in 0..3) holds inputs k = 128g + 32s + 8a + i (i = 0..7), input i at bit 4 (i / 2) + 16 (i % 2).
+ * A stack of n matrices [K, rows]: codes [n, rows, K / 8] uint32, scales [n, K / 128, rows] fp32
+ * (device). */
 typedef struct {
     const uint32_t *codes;
     const float *scales;
@@ -260,15 +262,15 @@ typedef struct {
 
 /* Layer weights with int4 experts; the router stays in the layer dtype (bf16). */
 typedef struct {
-    const void *w_router;      /* [N, d] bf16 */
+    const void *w_router;      /* [d, N] bf16 */
     const float *logit_bias;   /* [N] fp32, or NULL */
-    moe_q4_matrix w_gate;      /* [N, d_ff, d]; unused for MOE_FFN_RELU2 */
-    moe_q4_matrix w_up;        /* [N, d_ff, d] (W1 for RELU2) */
-    moe_q4_matrix w_down;      /* [N, d, d_ff] */
+    moe_q4_matrix w_gate;      /* quantised [N, d, d_ff]: codes [N, d_ff, d/8]; unused for RELU2 */
+    moe_q4_matrix w_up;        /* quantised [N, d, d_ff] (W1 for RELU2) */
+    moe_q4_matrix w_down;      /* quantised [N, d_ff, d]: codes [N, d, d_ff/8] */
     moe_q4_matrix sh_gate, sh_up, sh_down;   /* shared expert, as the routed ones */
 } moe_weights_q4;
 
-/* Quantise n_mats bf16 matrices w [n_mats, rows, K] (device) to the format above.
+/* Quantise n_mats bf16 matrices w [n_mats, K, rows] (device, x W orientation) to the format above.
  * K % 128 == 0 (MOE_ERR_UNSUPPORTED otherwise). */
 moe_status moe_quantize_q4(const void *w, int32_t n_mats, int32_t rows, int32_t K, uint32_t *codes,
                            float *scales, moe_stream_t stream);

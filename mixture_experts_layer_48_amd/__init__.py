@@ -246,10 +246,10 @@ def moe_ep_unpack(G: int, max_rows: int, row_bytes: int, recv_offsets, recv_inv,
 
 
 def moe_quantize_q4(w, codes, scales, stream=None) -> None:
-    """w: bf16 device tensor [n_mats, rows, K] (or [rows, K]); codes uint32-sized [.., rows, K/8]
-    (int32 storage is fine); scales fp32 [n_mats, K/128, rows]."""
+    """w: bf16 device tensor [n_mats, K, rows] (or [K, rows]; the x W orientation); codes
+    uint32-sized [.., rows, K/8] (int32 storage is fine); scales fp32 [n_mats, K/128, rows]."""
     shape = tuple(w.shape)
-    n_mats, rows, K = (1,) + shape if len(shape) == 2 else shape
+    n_mats, K, rows = (1,) + shape if len(shape) == 2 else shape
     _check(load_library().moe_quantize_q4(_ptr(w), n_mats, rows, K, _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_quantize_q4")
 
@@ -292,7 +292,7 @@ def quantize_weights_q4(weights: Dict, stream=None) -> Dict:
         if w is None:
             continue
         shape = tuple(w.shape)
-        n_mats, rows, K = (1,) + shape if len(shape) == 2 else shape
+        n_mats, K, rows = (1,) + shape if len(shape) == 2 else shape
         codes = torch.empty((n_mats, rows, K // 8), dtype=torch.int32, device=w.device)
         scales = torch.empty((n_mats, K // 128, rows), dtype=torch.float32, device=w.device)
         moe_quantize_q4(w, codes, scales, stream=stream)

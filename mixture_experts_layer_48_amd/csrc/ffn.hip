@@ -30,9 +30,9 @@ struct FfnKArgs {
     const bf16* A;          // in: x [T, d]; out: H [rows, d_ff]
     const int32_t* perm;
     const int32_t* offsets;
-    const bf16* B0;         // routed weights [N, Ncols, K] (gate for SwiGLU, else W)
+    const bf16* B0;         // routed weights [N, K, Ncols], K-major (gate for SwiGLU, else W)
     const bf16* B1;         // routed up weights (SwiGLU) or null
-    const bf16* S0;         // shared expert [Ncols, K] or null
+    const bf16* S0;         // shared expert [K, Ncols] or null
     const bf16* S1;
     const float* row_scale; // [T*k] or null (out-projection only)
     void* C;                // [rows, Ncols]: bf16 H (in-projection) or fp32 y_perm (out-projection)
@@ -204,6 +204,22 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
     return (const char*)(((unsigned long long)hi << 32) | lo);
 }
 
+// Eight bf16 of one column and eight consecutive k-rows of a K-major LDS tile: two transposed
+// 8-byte reads (ds_read_b64_tr_b16), rows 0-3 at byte `off` of the LDS array `base` and rows 4-7
+// at off + second.  Within each group of 16 lanes, lane j receives element j & 3 of the 8 bytes
+// addressed by lane 4 e + (j >> 2), for e = 0..3: with lane L addressing row (L >> 2) at column
+// 4 (L & 3), lane j gets column j of the four rows.
+// The address is one offset from the array itself: the compiler then still knows which LDS
+// array each read touches, and need not wait for direct loads in flight into another one.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+__device__ __forceinline__ bf16x8 lds_read_tr_b16x8(const void* base, int off, int second) {
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)((const char*)base + off));
+    const bf16x4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)((const char*)base + (off + second)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 struct TileInfo {
     int seg, mt, nt, kpart, row_beg, row_end;
 };
@@ -247,6 +263,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     constexpr int A_INS = BM / (8 * NW);             // load instructions per wave per stage (A)
     constexpr int B_INS = Cfg::BROWS / (8 * NW);     // (B)
     static_assert(BM % (8 * NW) == 0 && Cfg::BROWS % (8 * NW) == 0, "load split");
+    // Weight tiles are stored K-major, as the weights are: per matrix 64 k-rows of BNH columns
+    constexpr int BROWB = 2 * BNH;                   // bytes of one k-row of a weight tile
+    constexpr int BMATB = 64 * BROWB;                // bytes of one matrix's tile per stage
+    static_assert(BMATB % (1024 * NW) == 0, "every B load instruction stays inside one matrix");
     static_assert(BM <= 64 * NW, "one thread per row of the A tile");
     // two stages in two distinct LDS objects, so the compiler can tell a fragment read of one
     // stage from the asynchronous loads into the other
@@ -336,16 +356,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     };
     uint32_t offA[A_INS], offB[B_INS];
     const char *baseB0, *baseB1;
+    // B load instruction i of this wave fills bytes 1024 (wave + NW i) .. +1023 of the B region:
+    // lane l the 16 bytes at 1024 (wave + NW i) + 16 l, i.e. k-row kr and chunk position p of one
+    // matrix's tile.  Position p of k-row kr holds the weight chunk (8 columns) p ^ 4 (kr & 3), so
+    // that a transposed fragment read (4 k-rows x 32 bytes per 16 lanes) finds the four rows in
+    // four different quarters of the banks.  Columns past the matrix (a partial last n-tile) load
+    // the tile's first chunk instead; their outputs are never stored.  The per-lane offset is
+    // (kr * Ncols + column) * 2 bytes from the expert's matrix (a matrix stays below 4 GiB, which
+    // the host checks); the stage's first k-row goes in the scalar offset.
     auto set_b = [&](const TileInfo& ti) {
         const int n0 = ti.nt * BNH;
         const int l = fresh_lane();
-        const uint32_t lc = (uint32_t)(((l & 7) ^ ((4 * wave + (l >> 4)) & 7)) * 8);
 #pragma unroll
         for (int i = 0; i < B_INS; ++i) {
-            const int br = 8 * (wave + NW * i) + (l >> 3);   // row of the B tile
-            const int n = n0 + (br % BNH);
+            const int qm = (1024 * (wave + NW * i) + 16 * l) % BMATB;
+            const int kr = qm / BROWB, pos = (qm % BROWB) >> 4;
+            const int n = n0 + 8 * (pos ^ (4 * (kr & 3)));
             const int nc = n < a.Ncols ? n : n0;
-            offB[i] = ((uint32_t)nc * (uint32_t)a.K + lc) * 2u;
+            offB[i] = ((uint32_t)kr * (uint32_t)a.Ncols + (uint32_t)nc) * 2u;
         }
         const bf16* B0 = (ti.seg < a.N) ? a.B0 + ti.seg * wstride : a.S0;
         const bf16* B1 = (NB == 2) ? ((ti.seg < a.N) ? a.B1 + ti.seg * wstride : a.S1) : B0;
@@ -370,18 +398,37 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     // swizzle only depends on the lane: row r, chunk c sits at r*64 + ((c ^ ((r >> 1) & 7)) << 3)
     const int fr = lane & 31, fh = lane >> 5, l7 = (fr >> 1) & 7;
     const int abase = (wm * 32 + fr) * 64;              // sub-tile i of this wave: i * WGM + wm
-    const int bbase = (BM + wn * Cfg::WTN + fr) * 64;
+    // Weight fragment (32 columns x 16 k, lane l: column l & 31, k 8 (l >> 5) .. +7) from the
+    // K-major tile by two transposed reads: in each 16-lane group g = l >> 4, lane L = l & 15
+    // addresses k-row 8 (g >> 1) + (L >> 2) (+4 for the second read) at column
+    // 16 (g & 1) + 4 (L & 3) of the fragment's block, and receives column 16 (g & 1) + L of the
+    // four rows.  Bytes from the stage's B region: (16 kk + 4 half) BROWB + brow + bcol[j].
+    // this lane's weight-fragment byte offset within a k-step of matrix 0, per 32-column block:
+    // one register each (so that a read's address is the stage array, one lane offset and
+    // constants, which lets the compiler keep track of the LDS array it reads)
+    int boff[TN];
+    {
+        const int gq = lane >> 4, lq = lane & 15;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int ncol = wn * Cfg::WTN + j * 32 + 16 * (gq & 1) + 4 * (lq & 3);
+            boff[j] = (8 * (gq >> 1) + (lq >> 2)) * BROWB + (((ncol >> 3) ^ (4 * (lq >> 2))) << 4) +
+                      ((ncol & 7) << 1);
+        }
+    }
     struct Frags { bf16x8 a[TM]; bf16x8 b[NB][TN]; };
     auto load_frags = [&](const bf16* st, int kk, Frags& f, auto nv) {
         const int xo = ((2 * kk + fh) ^ l7) << 3;
 #pragma unroll
         for (int i = 0; i < decltype(nv)::value; ++i)
             f.a[i] = *(const bf16x8*)(st + abase + i * WGM * 32 * 64 + xo);
+        // lane-derived parts recomputed here (a few integer operations) rather than held in
+        // registers through the whole kernel
 #pragma unroll
-        for (int m = 0; m < NB; ++m)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                f.b[m][j] = *(const bf16x8*)(st + bbase + (m * BNH + j * 32) * 64 + xo);
+            for (int m = 0; m < NB; ++m)
+                f.b[m][j] = lds_read_tr_b16x8(st, BM * 128 + 16 * kk * BROWB + m * BMATB + boff[j], 4 * BROWB);
     };
     // The weight fragment is the MFMA's first operand and the row fragment its second, so each
     // accumulator holds the transposed 32x32 block: lane l has tile row (l & 31), register r
@@ -439,9 +486,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
                 buffer_load_lds16(baseA, (lds_void_t*)(st + (8 * (wave + NW * q)) * 64), offA[q], 2 * k0);
             } else {
                 const int i = q - A_INS;
-                const int br0 = 8 * NW * i;
-                const char* bb = uniform_ptr((NB == 2 && br0 >= BNH) ? baseB1 : baseB0);
-                buffer_load_lds16(bb, (lds_void_t*)(st + (BM + 8 * (wave + NW * i)) * 64), offB[i], 2 * k0);
+                const bool second = NB == 2 && (1024 * NW * i) / BMATB == 1;   // the up matrix
+                const char* bb = uniform_ptr(second ? baseB1 : baseB0);
+                buffer_load_lds16(bb, (lds_void_t*)((char*)st + BM * 128 + 1024 * (wave + NW * i)), offB[i],
+                                  2 * k0 * a.Ncols);
             }
         }
     };
@@ -452,7 +500,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     // this stage has just released.
     auto stage = [&](Acc& acc, bf16* cur_st, bf16* nxt_st, int k_next, int k_after, Frags& f0, Frags& f1, auto nv,
                      auto first) {
-        constexpr int NDS = decltype(nv)::value + NB * TN;   // fragment reads per K=16 step
+        constexpr int NDS = decltype(nv)::value + 2 * NB * TN;   // fragment reads per K=16 step
         load_frags(cur_st, 1, f1, nv);
         issue_part(nxt_st, k_next, NLD0, NLD, nv);
         mfmas(acc, f0, nv, first);
@@ -650,23 +698,49 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
 // ------------------------------------------------------------------ skinny path (decode)
 // For a few rows per expert the GEMMs are weight streams: every weight byte of a touched expert
 // is read once and used for at most 16 rows.  One wave owns CG 16-column groups of one segment
-// and the whole K range; its B fragments (16 weight rows x 32 K for v_mfma_f32_16x16x32_bf16)
-// come straight from memory into registers, U steps at a time, and its A fragments (the <= 16
-// rows, gathered through perm for the in-projection) serve all CG groups and are shared by all
-// waves through L2.  Waves are numbered segment, then column group, so the waves of a block
-// stream neighbouring weight rows.  Empty experts are skipped, so only touched
-// experts' weights are read.  Segments with more than 16 rows loop over 16-row tiles.  (Weight
-// loads stay cached: a load instruction covers half of each 128-byte line it touches and the
-// next K step reads the other half; non-temporal loads measured slower.)
+// and the whole K range.  Per K step of 32, its weight block (32 k-rows x 16 CG columns, K-major
+// as stored) comes from memory into registers U steps ahead, 16 bytes per lane (so the wave reads
+// whole 32 CG-byte segments of k-rows), is written to a small LDS tile of the wave's own and read
+// back as v_mfma_f32_16x16x32_bf16 B fragments (lane: column lane & 15, k 8 (lane >> 4) .. +7) by
+// transposed reads.  The A fragments (the <= 16 rows, gathered through perm for the
+// in-projection) serve all CG groups and are shared by all waves through L2.  Waves are numbered
+// segment, then column group, so the waves of a block stream neighbouring weight columns.
+// Empty experts are skipped, so only touched experts' weights are read.  Segments with more than
+// 16 rows loop over 16-row tiles.
+//
+// The wave's LDS tile holds 32 k-rows of 32 CG bytes.  A transposed read takes rows 8g .. 8g+3
+// (+4) of one 16-column block in lane group g = lane >> 4, and groups 0-1 (and 2-3) share an LDS
+// cycle.  So that the 8 rows of a cycle fall in distinct banks: with CG = 1 the blocks of 8 rows
+// (256 bytes) start 384 bytes apart (rows of blocks 1 and 3 in banks 32-63, of blocks 0 and 2 in
+// banks 0-31); with CG = 2 the 16-byte chunks of rows 8-15 and 24-31 are swapped in pairs (chunk
+// c at c ^ 2); with CG = 4 chunk c of row r sits at c ^ 2 (((r >> 1) & 1) | ((r >> 3) & 1) << 1).
+// Steps alternate between two tiles; a wave's LDS operations are performed in order, so a step's
+// writes into a tile follow the reads of the step two before.
+template <int CG>
+struct SkinnyTile {
+    static constexpr int ROWB = 32 * CG;                         // bytes of one k-row
+    static constexpr int BYTES = CG == 1 ? 3 * 384 + 256 : 32 * ROWB;
+    static constexpr int CPR = ROWB / 16;                        // 16-byte chunks per k-row
+    static constexpr int RPI = 64 / CPR;                         // k-rows per wave load
+    static_assert(CG == 1 || CG == 2 || CG == 4, "tile layouts for 1, 2 or 4 16-column groups");
+    __device__ static int off(int r, int c) {
+        if (CG == 1) return (r >> 3) * 384 + (r & 7) * ROWB + c * 16;
+        if (CG == 2) return r * ROWB + ((c ^ (2 * ((r >> 3) & 1))) << 4);
+        return r * ROWB + ((c ^ (2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)))) << 4);
+    }
+};
+
 template <int MODE, int U, int CG>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
+    using Tile = SkinnyTile<CG>;
     constexpr int NB = (MODE == MODE_IN_SWIGLU) ? 2 : 1;
-    const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);        // global wave id
+    __shared__ __attribute__((aligned(16))) char s_tile[4][2][NB][Tile::BYTES];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int gw = blockIdx.x * 4 + wv;                        // global wave id
     const int ngroups = (a.Ncols + 16 * CG - 1) / (16 * CG);
     const int nseg = a.N + (a.has_shared ? 1 : 0);
     const int seg = gw / ngroups, cg = gw % ngroups;
-    if (seg >= nseg) return;
+    if (seg >= nseg) return;                                   // no block barrier below
     int row_beg, row_end;
     const bf16 *B0, *B1 = nullptr;
     const size_t wstride = (size_t)a.Ncols * a.K;
@@ -683,17 +757,25 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
     }
     if (row_end <= row_beg) return;                             // expert not touched
     const int KS = a.K / 32;
-    const int kq = (lane >> 4) * 8;                             // this lane's K offset in a step
-    // this lane's B columns: one per 16-column group of the wave
-    const bf16* pb0[CG];
-    const bf16* pb1[CG];
+    const size_t step = (size_t)32 * a.Ncols;                   // elements between K steps
+    // this lane's weight loads (CG per matrix and step): k-row q RPI + lane / CPR, chunk lane % CPR
+    // of the wave's columns (Ncols is a multiple of 64, so every column group is whole); where they
+    // go in the tile; and where its transposed reads start
+    const bf16* pw0[CG];
+    const bf16* pw1[CG];
+    int woff[CG], roff[CG];
 #pragma unroll
-    for (int c = 0; c < CG; ++c) {
-        const int col = (cg * CG + c) * 16 + (lane & 15);
-        const int colc = col < a.Ncols ? col : a.Ncols - 1;
-        pb0[c] = B0 + (size_t)colc * a.K + kq;
-        pb1[c] = (NB == 2) ? B1 + (size_t)colc * a.K + kq : nullptr;
+    for (int q = 0; q < CG; ++q) {
+        const int r = q * Tile::RPI + lane / Tile::CPR, c = lane % Tile::CPR;
+        const size_t o = (size_t)r * a.Ncols + (size_t)cg * 16 * CG + 8 * c;
+        pw0[q] = B0 + o;
+        pw1[q] = (NB == 2) ? B1 + o : nullptr;
+        woff[q] = Tile::off(r, c);
+        const int g = lane >> 4, L = lane & 15;
+        roff[q] = Tile::off(8 * g + (L >> 2), 2 * q + ((L & 3) >> 1)) + (L & 1) * 8;
     }
+
+    const int kq = (lane >> 4) * 8;                             // this lane's K offset in a step
     for (int m0 = row_beg; m0 < row_end; m0 += 16) {
         const int r = m0 + (lane & 15);                         // this lane's A row
         const bool rok = r < row_end;
@@ -708,37 +790,66 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
             acc1[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
         const bf16x8 zero8 = {};
+        // a K step's weight pieces into tile t, and back as B fragments
+        struct Frag { bf16x8 b0[CG], b1[CG]; };
+        auto to_tile = [&](int t, const u32x4 (&w0)[CG], const u32x4 (&w1)[CG]) {
+#pragma unroll
+            for (int q = 0; q < CG; ++q) {
+                *(u32x4*)(s_tile[wv][t][0] + woff[q]) = w0[q];
+                if (NB == 2) *(u32x4*)(s_tile[wv][t][NB - 1] + woff[q]) = w1[q];
+            }
+        };
+        auto from_tile = [&](int t, Frag& f) {
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+                f.b0[c] = lds_read_tr_b16x8(s_tile, ((wv * 2 + t) * NB) * Tile::BYTES + roff[c], 4 * Tile::ROWB);
+                if (NB == 2)
+                    f.b1[c] = lds_read_tr_b16x8(s_tile, ((wv * 2 + t) * NB + 1) * Tile::BYTES + roff[c],
+                                                4 * Tile::ROWB);
+            }
+        };
+        auto mfmas = [&](const Frag& f, const bf16x8& av) {
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+                acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, f.b0[c], acc0[c], 0, 0, 0);
+                if (NB == 2) acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, f.b1[c], acc1[c], 0, 0, 0);
+            }
+        };
         int ks = 0;
         for (; ks + U <= KS; ks += U) {
-            bf16x8 b0[U][CG], b1[U][CG], av[U];
+            u32x4 w0[U][CG], w1[U][CG];
+            bf16x8 av[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
-                for (int c = 0; c < CG; ++c) {
-                    b0[u][c] = *(const bf16x8*)(pb0[c] + (ks + u) * 32);
-                    if (NB == 2) b1[u][c] = *(const bf16x8*)(pb1[c] + (ks + u) * 32);
+                for (int q = 0; q < CG; ++q) {
+                    w0[u][q] = *(const u32x4*)(pw0[q] + (ks + u) * step);
+                    if (NB == 2) w1[u][q] = *(const u32x4*)(pw1[q] + (ks + u) * step);
                 }
                 av[u] = rok ? *(const bf16x8*)(pa + (ks + u) * 32) : zero8;
             }
+            // every step's tile write and read go out before the MFMAs (steps alternate tiles)
+            Frag f[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; ++u) {
+                to_tile(u & 1, w0[u], w1[u]);
+                from_tile(u & 1, f[u]);
+            }
 #pragma unroll
-                for (int c = 0; c < CG; ++c) {
-                    acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b0[u][c], acc0[c], 0, 0, 0);
-                    if (NB == 2) acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], b1[u][c], acc1[c], 0, 0, 0);
-                }
+            for (int u = 0; u < U; ++u) mfmas(f[u], av[u]);
         }
         for (; ks < KS; ++ks) {
-            const bf16x8 av = rok ? *(const bf16x8*)(pa + ks * 32) : zero8;
+            u32x4 w0[CG], w1[CG];
 #pragma unroll
-            for (int c = 0; c < CG; ++c) {
-                const bf16x8 b0 = *(const bf16x8*)(pb0[c] + ks * 32);
-                acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0, acc0[c], 0, 0, 0);
-                if (NB == 2) {
-                    const bf16x8 b1 = *(const bf16x8*)(pb1[c] + ks * 32);
-                    acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1, acc1[c], 0, 0, 0);
-                }
+            for (int q = 0; q < CG; ++q) {
+                w0[q] = *(const u32x4*)(pw0[q] + ks * step);
+                if (NB == 2) w1[q] = *(const u32x4*)(pw1[q] + ks * step);
             }
+            const bf16x8 av = rok ? *(const bf16x8*)(pa + ks * 32) : zero8;
+            Frag f;
+            to_tile(ks & 1, w0, w1);
+            from_tile(ks & 1, f);
+            mfmas(f, av);
         }
         // 16x16 C layout: lane holds column (lane & 15), rows 4 * (lane >> 4) + i
 #pragma unroll
@@ -776,8 +887,8 @@ static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
 // all of its waves to be resident at once (two groups: 0.38 vs 0.35 ms); the out-projection
 // takes two groups per wave, which halves its activation loads (0.17 vs 0.18 ms; four groups
 // leave too few waves for d = 4096).
-#define SK_U_IN 4
-#define SK_CG_IN 1
+#define SK_U_IN 2
+#define SK_CG_IN 4
 #define SK_U_OUT 4
 #define SK_CG_OUT 2
 static bool skinny(const FfnLaunch& f) { return (long long)f.T * f.k <= 16LL * f.N; }
@@ -818,14 +929,13 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
     const float* ar;
     if (MODE == MODE_OUT) ar = A + (size_t)r * K;
     else ar = A + (size_t)((seg < N) ? perm[r] / k : r - T * k) * K;
-    const float* wr0 = w0 + (size_t)c * K;
+    // weights K-major: column c of a [K, Ncols] matrix
     float s0 = 0.f;
-    for (int i = 0; i < K; ++i) s0 = fmaf(ar[i], wr0[i], s0);
+    for (int i = 0; i < K; ++i) s0 = fmaf(ar[i], w0[(size_t)i * Ncols + c], s0);
     float v;
     if (MODE == MODE_IN_SWIGLU) {
-        const float* wr1 = w1 + (size_t)c * K;
         float s1 = 0.f;
-        for (int i = 0; i < K; ++i) s1 = fmaf(ar[i], wr1[i], s1);
+        for (int i = 0; i < K; ++i) s1 = fmaf(ar[i], w1[(size_t)i * Ncols + c], s1);
         v = s0 / (1.0f + expf(-s0)) * s1;
     } else if (MODE == MODE_IN_RELU) {
         v = fmaxf(s0, 0.f);

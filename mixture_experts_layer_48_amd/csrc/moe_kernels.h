@@ -33,10 +33,10 @@ struct FfnLaunch {
     const void* x;            // [T, d]
     const int32_t* perm;      // [T*k]
     const int32_t* offsets;   // [N+1]
-    const void* w_gate;       // [N, d_ff, d] or null
-    const void* w_up;         // [N, d_ff, d]
-    const void* w_down;       // [N, d, d_ff]
-    const void* sh_gate;      // [d_ff, d] or null
+    const void* w_gate;       // [N, d, d_ff] or null (x W orientation: K-major)
+    const void* w_up;         // [N, d, d_ff]
+    const void* w_down;       // [N, d_ff, d]
+    const void* sh_gate;      // [d, d_ff] or null
     const void* sh_up;
     const void* sh_down;
     const float* row_scale;   // [T*k] or null
@@ -69,7 +69,7 @@ hipError_t launch_ep_receive_layout(const int32_t* recv_counts, int N, int G, co
 hipError_t launch_ep_unpack(const void* y_grouped, const int32_t* recv_inv, const int32_t* recv_offsets, int G,
                             int max_rows, int row_bytes, void* ret, hipStream_t s);
 
-// Int4 expert weights: quantisation of n_mats bf16 matrices [rows, K] (K % 128 == 0), and the
+// Int4 expert weights: quantisation of n_mats bf16 matrices [K, rows] (K % 128 == 0), and the
 // weight-streaming expert FFN on int4 weights (f.q4; the out-projection always in one K part).
 hipError_t launch_q4_quantize(const void* w, long long n_mats, int rows, int K, uint32_t* codes, float* scales,
                               hipStream_t s);

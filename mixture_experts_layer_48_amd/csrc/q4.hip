@@ -3,7 +3,8 @@
 // The pages name INT4 (GPTQ/AWQ) expert weights at a quarter of the memory (page "大模型MoE混合专家
 // 架构原理与DeepSeek-V4工程实践解析", section DeepSeek-V4的MoE架构工程细节) without a format; the one
 // used here:
-//   per weight row and group of 128 consecutive inputs, scale = amax / 7 (fp32) and
+//   per output (a column of the [K, rows] weight matrix, a row of the codes) and group of 128
+//   consecutive inputs, scale = amax / 7 (fp32) and
 //   q = clamp(rint(w / scale), -8, 7) (fp32 division, ties to even; an all-zero group has scale 0
 //   and q = 0); the weight it stands for is scale * q.
 //   codes q + 8, four bits each, eight to a uint32: within row r and group g, word a*4 + s
@@ -23,41 +24,47 @@ enum { MODE_IN_SWIGLU = 0, MODE_IN_RELU = 1, MODE_OUT = 2 };
 constexpr int Q4G = 128;   // inputs per scale group
 
 // ------------------------------------------------------------------ quantisation
-// One wave per (row, group): lane l holds inputs 2l and 2l + 1 of the group.
-__global__ __launch_bounds__(256) void q4_quantize_kernel(const bf16* __restrict__ w, long long n_rows, int rows,
+// Input: n_mats bf16 matrices [K, rows] (x W orientation: column r holds output r's weights).
+// One wave per 64 consecutive columns and one group of 128 inputs: lane l takes column r0 + l,
+// reads its 128 inputs (each read of the wave is 128 contiguous bytes of one k-row), finds the
+// group's scale and codes in fp32 and writes its 16 code words and its scale.
+__global__ __launch_bounds__(256) void q4_quantize_kernel(const bf16* __restrict__ w, long long n_mats, int rows,
                                                           int K, uint32_t* __restrict__ codes,
                                                           float* __restrict__ scales) {
-    const int G = K / Q4G;
+    const int G = K / Q4G, RB = (rows + 63) / 64;
     const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= n_rows * G) return;
+    if (wid >= n_mats * RB * G) return;
     const int lane = threadIdx.x & 63;
-    const long long row = wid / G;
-    const int g = (int)(wid % G);
-    const bf16* src = w + row * K + (long long)g * Q4G + 2 * lane;
-    const float v0 = (float)src[0], v1 = (float)src[1];
-    float amax = fmaxf(fabsf(v0), fabsf(v1));
+    const long long mat = wid / ((long long)RB * G);
+    const int rem = (int)(wid % ((long long)RB * G));
+    const int g = rem % G, r = (rem / G) * 64 + lane;
+    if (r >= rows) return;
+    const bf16* src = w + (size_t)mat * K * rows + (size_t)g * Q4G * rows + r;
+    float v[Q4G];
+    float amax = 0.0f;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, WAVE));
-    int q0 = 0, q1 = 0;
+    for (int i = 0; i < Q4G; ++i) {
+        v[i] = (float)src[(size_t)i * rows];
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
     float sc = 0.0f;
-    if (amax > 0.0f) {
-        sc = __fdiv_rn(amax, 7.0f);
-        q0 = (int)fminf(fmaxf(rintf(__fdiv_rn(v0, sc)), -8.0f), 7.0f);
-        q1 = (int)fminf(fmaxf(rintf(__fdiv_rn(v1, sc)), -8.0f), 7.0f);
-    }
-    // inputs 2l, 2l + 1 are i = 2 (l % 4), i + 1 of word (a, s) = ((l % 16) / 4, l / 16)
-    const int sh = 4 * (lane & 3);
-    uint32_t part = ((uint32_t)(q0 + 8) << sh) | ((uint32_t)(q1 + 8) << (16 + sh));
-    part |= __shfl_xor(part, 1, WAVE);
-    part |= __shfl_xor(part, 2, WAVE);
-    if ((lane & 3) == 0) {
-        const int word = 4 * ((lane & 15) >> 2) + (lane >> 4);
-        codes[row * (K / 8) + (long long)g * 16 + word] = part;
-    }
-    if (lane == 0) {
-        const long long mat = row / rows, r = row % rows;
-        scales[(mat * G + g) * rows + r] = sc;
-    }
+    if (amax > 0.0f) sc = __fdiv_rn(amax, 7.0f);
+    // word a*4 + s of the group holds inputs 32 s + 8 a + i, input i at bit 4 (i / 2) + 16 (i % 2)
+    uint32_t* out = codes + ((size_t)mat * rows + r) * (K / 8) + (size_t)g * 16;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                int q = 0;
+                if (amax > 0.0f) q = (int)fminf(fmaxf(rintf(__fdiv_rn(v[32 * s + 8 * a + i], sc)), -8.0f), 7.0f);
+                word |= (uint32_t)(q + 8) << (4 * (i >> 1) + 16 * (i & 1));
+            }
+            out[4 * a + s] = word;
+        }
+    scales[((size_t)mat * G + g) * rows + r] = sc;
 }
 
 // ------------------------------------------------------------------ weight-streaming FFN
@@ -239,10 +246,9 @@ hipError_t launch_q4(const FfnQ4Args& a, hipStream_t s) {
 
 hipError_t launch_q4_quantize(const void* w, long long n_mats, int rows, int K, uint32_t* codes, float* scales,
                               hipStream_t s) {
-    const long long n_rows = n_mats * rows;
-    const long long waves = n_rows * (K / Q4G);
+    const long long waves = n_mats * ((rows + 63) / 64) * (K / Q4G);
     if (waves == 0) return hipSuccess;
-    q4_quantize_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>((const bf16*)w, n_rows, rows, K, codes, scales);
+    q4_quantize_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>((const bf16*)w, n_mats, rows, K, codes, scales);
     return hipGetLastError();
 }
 

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
         const int e = e0 + c * 16 + (lane & 15);
-        pb[c] = wr + (size_t)(e < N ? e : 0) * d + koff;
+        pb[c] = wr + (size_t)koff * N + (e < N ? e : 0);     // w_router [d, N]: column e
     }
     double acc64[NCT][2][4];
     f32x4 acc[NCT][2];
@@ -93,7 +93,9 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
         f.a0 = *(const bf16x8*)(pa0 + k);
         f.a1 = *(const bf16x8*)(pa1 + k);
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) f.b[c] = *(const bf16x8*)(pb[c] + k);
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f.b[c][i] = pb[c][(size_t)(k + i) * N];
     };
     auto mma = [&](const Frag& f) {
 #pragma unroll
@@ -173,12 +175,12 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(
     if (o >= (long long)T * N) return;
     const int t = (int)(o / N), e = (int)(o % N);
     const float* xr = x + (size_t)t * d;
-    const float* wv = wr + (size_t)e * d;
+    const float* wv = wr + e;                                // w_router [d, N]: column e
     double acc = 0.0;
     for (int kc = 0; kc < d; kc += RL_CHUNK) {
         float s = 0.f;
         const int kend = min(kc + RL_CHUNK, d);
-        for (int i = kc; i < kend; ++i) s = fmaf(xr[i], wv[i], s);
+        for (int i = kc; i < kend; ++i) s = fmaf(xr[i], wv[(size_t)i * N], s);
         acc += (double)s;
     }
     if (bias) acc += (double)bias[e];

@@ -70,13 +70,14 @@ def _f64(a) -> np.ndarray:
 
 # ---------------------------------------------------------------- step 1
 def router_logits(x, w_router, logit_bias=None) -> np.ndarray:
-    """z[t, e] = sum_i x[t, i] * w_router[e, i]  (+ b[e]).
+    """z[t, e] = sum_i x[t, i] * w_router[i, e]  (+ b[e]).
 
     The router is a learned linear layer giving one score per expert
-    ([P1] 什麼是 MoE 模型; [P2] 深入原理; [P5] §2.2).  w_router is stored
-    output-major [N, d].  The optional bias b[e] is part of the logit.
+    ([P1] 什麼是 MoE 模型; [P2] 深入原理; [P5] §2.2).  w_router is [d, N],
+    the toy's router_W ([P2] 代码: gate = x @ router_W).  The optional bias
+    b[e] is part of the logit.
     """
-    z = _f64(x) @ _f64(w_router).T
+    z = _f64(x) @ _f64(w_router)
     if logit_bias is not None:
         z = z + _f64(logit_bias)[None, :]
     return z
@@ -222,18 +223,18 @@ def expert_ffn(xr, w_up, w_down, ffn: str, w_gate=None) -> np.ndarray:
     """One expert's FFN on rows xr [M, d]: two linear maps with an activation
     between them ([P1] 什麼是 MoE 模型), no biases.
 
-    RELU2:  relu(xr W1) W2, W1 = w_up [d_ff, d], W2 = w_down [d, d_ff]
-    SWIGLU: (silu(xr Wg) * (xr Wu)) Wd, Wg/Wu [d_ff, d], Wd [d, d_ff]
-    (weights stored output-major, so x W means x @ w.T)
+    RELU2:  relu(xr W1) W2, W1 = w_up [d, d_ff], W2 = w_down [d_ff, d]
+    SWIGLU: (silu(xr Wg) * (xr Wu)) Wd, Wg/Wu [d, d_ff], Wd [d_ff, d]
+    (the x W orientation of the toy's x @ experts_W[e], [P2] 代码)
     """
     xr = _f64(xr)
     if ffn == RELU2:
-        h = np.maximum(xr @ _f64(w_up).T, 0.0)
+        h = np.maximum(xr @ _f64(w_up), 0.0)
     elif ffn == SWIGLU:
-        h = silu(xr @ _f64(w_gate).T) * (xr @ _f64(w_up).T)
+        h = silu(xr @ _f64(w_gate)) * (xr @ _f64(w_up))
     else:
         raise ValueError(f"unknown ffn {ffn!r}")
-    return h @ _f64(w_down).T
+    return h @ _f64(w_down)
 
 
 # ---------------------------------------------------------------- step 7
@@ -257,9 +258,10 @@ def forward(x, w_router, w_up, w_down, k: int, ffn: str, gating: str, w_gate=Non
             tokens: Optional[Sequence[int]] = None, z=None) -> Dict[str, np.ndarray]:
     """The whole layer forward, steps 1-7.
 
-    Expert weights are indexed per expert (w_up[e], w_down[e], w_gate[e]);
-    any object that returns one expert's array on indexing works, so large
-    weight sets can be converted to float64 one expert at a time.
+    x [T, d]; w_router [d, N].  Expert weights are indexed per expert
+    (w_gate[e], w_up[e] [d, d_ff], w_down[e] [d_ff, d]); any object that
+    returns one expert's array on indexing works, so large weight sets can be
+    converted to float64 one expert at a time.
     shared = (sh_gate, sh_up, sh_down) or None.
     tokens: evaluate the FFN/combine only for these tokens (routing always
     covers every token, since capacity couples them).
@@ -369,19 +371,21 @@ Q4_GROUP = 128      # input features per scale group
 
 
 def quantize_q4(w):
-    """Weight-only int4 quantisation of one weight matrix [rows, K] (the
-    pages name GPTQ/AWQ INT4 expert weights at a quarter of the memory, [P3]
+    """Weight-only int4 quantisation of one weight matrix w [K, rows] in the
+    x W orientation (K inputs, one column per output; the pages name
+    GPTQ/AWQ INT4 expert weights at a quarter of the memory, [P3]
     DeepSeek-V4的MoE架构工程细节 and [P5] §3.1's AWQ deployment, and give no
     format; this one is defined here).
 
-    Per row and group of Q4_GROUP consecutive inputs: scale = amax / 7 with
-    amax the largest |w| of the group, and q = clamp(rint(w / scale), -8, 7)
-    (round half to even); an all-zero group has scale 0 and q = 0.  The
-    scale and the division are taken in fp32, the precision in which the
-    kernel decides the codes.  Returns q [rows, K] int8 and scales
-    [rows, K / Q4_GROUP] fp32.  The weight it stands for is scale * q.
+    Per output (row of the result) and group of Q4_GROUP consecutive inputs:
+    scale = amax / 7 with amax the largest |w| of the group, and
+    q = clamp(rint(w / scale), -8, 7) (round half to even); an all-zero group
+    has scale 0 and q = 0.  The scale and the division are taken in fp32, the
+    precision in which the kernel decides the codes.  Returns q [rows, K] int8
+    (one row per output) and scales [rows, K / Q4_GROUP] fp32.  The weight it
+    stands for is scale * q (dequantize_q4).
     """
-    w = np.asarray(w, dtype=np.float32)
+    w = np.asarray(w, dtype=np.float32).T
     rows, K = w.shape
     blk = w.reshape(rows, K // Q4_GROUP, Q4_GROUP)
     amax = np.max(np.abs(blk), axis=2)                              # [rows, groups], exact
@@ -393,11 +397,11 @@ def quantize_q4(w):
 
 
 def dequantize_q4(q, scales):
-    """The weight an int4 matrix stands for: scale[r, g] * q[r, k] for k in
-    group g, exactly (float64)."""
+    """The weight matrix [K, rows] (x W orientation) an int4 matrix stands for:
+    element (k, r) = scale[r, g] * q[r, k] for k in group g, exactly (float64)."""
     q = np.asarray(q, dtype=np.float64)
     sc = np.repeat(np.asarray(scales, dtype=np.float64), Q4_GROUP, axis=1)
-    return sc * q
+    return (sc * q).T
 
 
 def pack_q4(q):

@@ -1,6 +1,13 @@
 """Shared helpers of the GPU parity tests: build a layer on the GPU from a
 seeded workload, run it through the C ABI, and hand the same input values to
-the CPU oracle (one expert at a time, converted to float64 on demand)."""
+the CPU oracle.
+
+The oracle is the plain C++ one (oracle/moe_oracle.cpp, through oracle.cpp) for
+the logits, the routing and the grouping of every case, and for the expert FFNs
+and the combine wherever their float64 work is small.  The full-size layers'
+FFNs (up to 6.5 TFLOP) take the NumPy oracle, whose steps use BLAS matrix
+products, one expert's weights at a time; both implementations are pinned by
+the same tests (tests/test_oracle_pins.py)."""
 from __future__ import annotations
 
 import math
@@ -14,6 +21,7 @@ import torch
 
 import mixture_experts_layer_48_amd as M
 import oracle as O
+import oracle.cpp as OC
 import workloads as W
 
 
@@ -31,12 +39,12 @@ def check_shapes(cfg: W.LayerConfig, inp: Dict) -> None:
     """Host-side check that every operand matches what the kernels assume."""
     T, d, N, dff = cfg.T, cfg.d, cfg.N, cfg.d_ff
     assert inp["x"].shape == (T, d) and inp["x"].is_contiguous()
-    assert inp["w_router"].shape == (N, d)
-    assert inp["w_up"].shape == (N, dff, d) and inp["w_down"].shape == (N, d, dff)
+    assert inp["w_router"].shape == (d, N)
+    assert inp["w_up"].shape == (N, d, dff) and inp["w_down"].shape == (N, dff, d)
     if cfg.ffn == W.FFN_SWIGLU:
-        assert inp["w_gate"].shape == (N, dff, d)
+        assert inp["w_gate"].shape == (N, d, dff)
     if cfg.has_shared:
-        assert inp["sh_up"].shape == (dff, d) and inp["sh_down"].shape == (d, dff)
+        assert inp["sh_up"].shape == (d, dff) and inp["sh_down"].shape == (dff, d)
     for key, t in inp.items():
         if t is not None and key != "logit_bias":
             assert t.dtype == cfg.torch_dtype and t.is_contiguous(), key
@@ -74,7 +82,23 @@ def run_layer(cfg: W.LayerConfig, inp: Dict, events=None):
     return layer, y, r
 
 
+# float64 FFN work above which the NumPy (BLAS) oracle evaluates the forward instead of the C++ one
+CPP_FFN_FLOPS = 5e10
+
+
 def oracle_forward(cfg: W.LayerConfig, inp: Dict, tokens=None, z=None):
+    n = cfg.T if tokens is None else len(tokens)
+    nm = 3 if cfg.ffn == W.FFN_SWIGLU else 2
+    flops = 2.0 * nm * cfg.d * cfg.d_ff * n * (cfg.k + (1 if cfg.has_shared else 0))
+    if flops <= CPP_FFN_FLOPS:
+        host = {key: (None if v is None else v.cpu()) for key, v in inp.items()}
+        shared = (host["sh_gate"], host["sh_up"], host["sh_down"]) if cfg.has_shared else None
+        log(f"[{cfg.name}] oracle: C++ ({flops / 1e9:.1f} GFLOP of FFN)")
+        return OC.forward(host["x"], host["w_router"], host["w_up"], host["w_down"], cfg.k, cfg.ffn, cfg.gating,
+                          w_gate=host["w_gate"], logit_bias=None if host["logit_bias"] is None
+                          else host["logit_bias"].numpy(), capacity_factor=cfg.capacity_factor, shared=shared,
+                          tokens=tokens, z=z)
+    log(f"[{cfg.name}] oracle: NumPy ({flops / 1e9:.0f} GFLOP of FFN)")
     shared = None
     if cfg.has_shared:
         shared = (None if inp["sh_gate"] is None else f64(inp["sh_gate"]), f64(inp["sh_up"]), f64(inp["sh_down"]))
@@ -139,13 +163,13 @@ def h_rounding_bound(cfg: W.LayerConfig, inp: Dict, idx: np.ndarray, w: np.ndarr
     for e in np.unique(idx[idx >= 0]):
         rows, slots = np.nonzero(idx == e)
         xr = x[rows]
-        u = xr @ f64(inp["w_up"][int(e)]).T
+        u = xr @ f64(inp["w_up"][int(e)])
         if cfg.ffn == W.FFN_SWIGLU:
-            g = xr @ f64(inp["w_gate"][int(e)]).T
+            g = xr @ f64(inp["w_gate"][int(e)])
             h = g / (1.0 + np.exp(-g)) * u
         else:
             h = np.maximum(u, 0.0)
-        out[rows] += np.abs(w[rows, slots])[:, None] * (np.abs(h) @ np.abs(f64(inp["w_down"][int(e)])).T)
+        out[rows] += np.abs(w[rows, slots])[:, None] * (np.abs(h) @ np.abs(f64(inp["w_down"][int(e)])))
     return out * 2.0 ** -9
 
 
@@ -157,12 +181,11 @@ U32 = 2.0 ** -24     # unit roundoff of fp32
 
 
 def oracle_logits(inp: Dict):
-    """The oracle's own float64 logits, and sum_i |x_i w_i| per logit (for the error bound)."""
-    x = f64(inp["x"])
-    wr = f64(inp["w_router"])
+    """The oracle's own float64 logits (C++ oracle), and sum_i |x_i w_i| per logit (for the error
+    bound)."""
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
-    z64 = O.router_logits(x, wr, bias)
-    s_abs = np.abs(x) @ np.abs(wr).T
+    z64 = OC.router_logits(inp["x"].cpu(), inp["w_router"].cpu(), bias)
+    s_abs = np.abs(f64(inp["x"])) @ np.abs(f64(inp["w_router"]))
     return z64, s_abs
 
 
@@ -225,7 +248,7 @@ def check_routing_vs_fp64(cfg: W.LayerConfig, rn: Dict[str, np.ndarray], z64: np
     Returns the oracle's idx and w and the mask of tokens routed alike."""
     C = O.expert_capacity(cfg.capacity_factor, cfg.T, cfg.k, cfg.N) if cfg.capacity_factor > 0 else 0
     gating = O.TOPK_SOFTMAX if cfg.gating == W.GATE_TOPK_SOFTMAX else O.SOFTMAX_TOPK
-    idx64, w64 = O.route_from_logits(z64, cfg.k, gating, C)
+    idx64, w64 = OC.route_from_logits(z64, cfg.k, gating, C)
     depth = near_tie_depth(cfg, idx64, z64)
     ties = set(O.near_tie_tokens(z64, depth, thr).tolist())
     alike = (rn["idx"] == idx64).all(axis=1)
@@ -257,7 +280,7 @@ def check_routing(cfg: W.LayerConfig, inp: Dict, rn: Dict[str, np.ndarray]):
     # two logits each off by at most zerr can swap only if their gap is below 2 * zerr
     idx64, _, alike = check_routing_vs_fp64(cfg, rn, z64, zerr, thr=max(1e-6, 2.0 * zerr))
     if alike.all():
-        counts, offsets, perm, inv = O.group_by_expert(idx64, cfg.N)
+        counts, offsets, perm, inv = OC.group_by_expert(idx64, cfg.N)
         assert np.array_equal(rn["counts"], counts) and np.array_equal(rn["offsets"], offsets)
         assert np.array_equal(rn["perm"][: offsets[-1]], perm) and np.array_equal(rn["inv"], inv)
     return z64, zerr, alike

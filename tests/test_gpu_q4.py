@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _gpu_quantize(w):
-    n, rows, K = w.shape
+    n, K, rows = w.shape                                        # x W orientation
     codes = torch.empty((n, rows, K // 8), dtype=torch.int32, device="cuda")
     scales = torch.empty((n, K // 128, rows), dtype=torch.float32, device="cuda")
     M.moe_quantize_q4(w, codes, scales)
@@ -37,8 +37,8 @@ def test_quantize_bit_exact(shape, seed):
     log(f"[q4 quantize] {shape}")
     cfg = W.LayerConfig("q", T=1, d=shape[2], N=shape[0], k=1, d_ff=shape[1], dtype="bf16", ffn=W.FFN_RELU2,
                         gating=W.GATE_TOPK_SOFTMAX, seed=seed)
-    w = W.make_inputs(cfg, "cuda")["w_up"]                      # [N, d_ff, d]
-    w[0, 3, :] = 0.0                                            # an all-zero row (all-zero groups)
+    w = W.make_inputs(cfg, "cuda")["w_up"]                      # [N, d, d_ff] = [mats, K, rows]
+    w[0, :, 3] = 0.0                                            # an all-zero column (all-zero groups)
     codes, scales = _gpu_quantize(w)
     wf = w.float().cpu().numpy()
     for m in range(shape[0]):
@@ -49,10 +49,10 @@ def test_quantize_bit_exact(shape, seed):
 
 def test_quantize_ties_and_grid():
     # amax 7 -> scale 1: halves round to even; values on the grid come back exactly
-    w = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((1, 128, 2), dtype=torch.bfloat16, device="cuda")      # [K, rows]
     vals = [7.0, 2.5, -0.5, 3.5, -2.5, 1.5, -7.0, 0.5]
-    w[0, 0, :8] = torch.tensor(vals)
-    w[0, 1, :] = 0.375
+    w[0, :8, 0] = torch.tensor(vals)
+    w[0, :, 1] = 0.375
     codes, scales = _gpu_quantize(w)
     oc, osc = _oracle_codes(w[0].float().cpu().numpy())
     assert np.array_equal(codes[0], oc) and np.array_equal(scales[0], osc.T)

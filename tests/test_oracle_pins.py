@@ -4,6 +4,10 @@ Nothing here compares the oracle with itself: each test checks it against a
 value the pages print, a closed form, brute force, a special case that
 reduces to a plain product written out with loops, or the independent
 capacity implementation in capacity_fixed_point.py.
+
+The oracle has two implementations, the plain C++ one (oracle/moe_oracle.cpp,
+through oracle.cpp) and the NumPy one (oracle.moe_oracle); every pin of a step
+both implement runs against each of them (the `impl` fixture).
 """
 import itertools
 import math
@@ -13,6 +17,7 @@ import numpy as np
 import pytest
 
 import oracle as O
+import oracle.cpp as OC
 from capacity_fixed_point import capacity_route_fixed_point
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -23,21 +28,27 @@ def _golden_rows(name):
         return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
 
 
+@pytest.fixture(params=["numpy", "cpp"])
+def impl(request):
+    """The oracle implementation under test: NumPy or the plain C++ one."""
+    return O if request.param == "numpy" else OC
+
+
 # ---------------------------------------------------------------- helpers written out with loops
-def naive_matmul_t(a, w):
-    """a [M, K] times w^T, w stored [Nout, K]; pure Python loops in float64."""
+def naive_matmul(a, w):
+    """a [M, K] times w [K, Nout]; pure Python loops in float64."""
     M, K = len(a), len(a[0])
-    return [[sum(float(a[m][i]) * float(w[n][i]) for i in range(K)) for n in range(len(w))] for m in range(M)]
+    return [[sum(float(a[m][i]) * float(w[i][n]) for i in range(K)) for n in range(len(w[0]))] for m in range(M)]
 
 
 def naive_ffn(x, w_up, w_down, ffn, w_gate=None):
     if ffn == O.RELU2:
-        h = [[max(v, 0.0) for v in row] for row in naive_matmul_t(x, w_up)]
+        h = [[max(v, 0.0) for v in row] for row in naive_matmul(x, w_up)]
     else:
-        g = naive_matmul_t(x, w_gate)
-        u = naive_matmul_t(x, w_up)
+        g = naive_matmul(x, w_gate)
+        u = naive_matmul(x, w_up)
         h = [[gv / (1.0 + math.exp(-gv)) * uv for gv, uv in zip(gr, ur)] for gr, ur in zip(g, u)]
-    return np.array(naive_matmul_t(h, w_down))
+    return np.array(naive_matmul(h, w_down))
 
 
 def naive_softmax(v):
@@ -49,10 +60,12 @@ def naive_softmax(v):
 
 def rand_layer(rng, T, d, N, d_ff, ffn):
     x = rng.standard_normal((T, d))
-    wr = rng.standard_normal((N, d)) / math.sqrt(d)
-    wg = rng.standard_normal((N, d_ff, d)) / math.sqrt(d) if ffn == O.SWIGLU else None
-    wu = rng.standard_normal((N, d_ff, d)) / math.sqrt(d)
-    wd = rng.standard_normal((N, d, d_ff)) / math.sqrt(d_ff)
+    wr = rng.standard_normal((d, N)) / math.sqrt(d)
+    wg = rng.standard_normal((N, d, d_ff)) / math.sqrt(d) if ffn == O.SWIGLU else None
+    wu = rng.standard_normal((N, d, d_ff)) / math.sqrt(d)
+    wd = rng.standard_normal((N, d_ff, d)) / math.sqrt(d_ff)
+    if ffn != O.SWIGLU:
+        wg = None
     return x, wr, wg, wu, wd
 
 
@@ -83,7 +96,7 @@ def test_param_counts_shared_expert_counts_as_always_active():
 
 # ---------------------------------------------------------------- worked combine (page 1, step 6)
 @pytest.mark.parametrize("gating", [O.TOPK_SOFTMAX, O.SOFTMAX_TOPK])
-def test_worked_combine_two_experts(gating):
+def test_worked_combine_two_experts(impl, gating):
     # Experts 2 and 5 get scores 0.6 and 0.4; the output is 0.6 E2(x) + 0.4 E5(x).
     # Expert e is relu(x I) (c_e I): on x > 0 it returns c_e * x exactly.
     N, d = 8, 4
@@ -94,20 +107,20 @@ def test_worked_combine_two_experts(gating):
     w_up = np.stack([np.eye(d)] * N)
     w_down = np.stack([c[e] * np.eye(d) for e in range(N)])
     x = np.array([[0.5, 1.0, 2.0, 3.0]])
-    out = O.forward(x, None, w_up, w_down, 2, O.RELU2, gating, z=z)
+    out = impl.forward(x, None, w_up, w_down, 2, O.RELU2, gating, z=z)
     assert out["idx"].tolist() == [[2, 5]]
     assert np.allclose(out["w"], [[0.6, 0.4]], atol=1e-12, rtol=0)
     assert np.allclose(out["y"], (0.6 * c[2] + 0.4 * c[5]) * x, atol=1e-12, rtol=0)
 
 
 # ---------------------------------------------------------------- top-k
-def test_topk_set_is_brute_force_best_subset_with_ties():
+def test_topk_set_is_brute_force_best_subset_with_ties(impl):
     rng = np.random.default_rng(5)
     for trial in range(40):
         N = int(rng.integers(1, 7))
         z = rng.integers(-2, 3, size=(30, N)).astype(np.float64)   # many exact ties
         for k in range(1, N + 1):
-            idx, _ = O.topk_route(z, k, O.TOPK_SOFTMAX)
+            idx, _ = impl.topk_route(z, k, O.TOPK_SOFTMAX)
             for t in range(z.shape[0]):
                 best = max(itertools.combinations(range(N), k),
                            key=lambda s: (sum(z[t, list(s)]), [-e for e in s]))
@@ -117,20 +130,20 @@ def test_topk_set_is_brute_force_best_subset_with_ties():
                     assert zs[j] > zs[j + 1] or (zs[j] == zs[j + 1] and idx[t, j] < idx[t, j + 1])
 
 
-def test_both_gating_modes_pick_the_same_experts():
+def test_both_gating_modes_pick_the_same_experts(impl):
     rng = np.random.default_rng(6)
     z = rng.standard_normal((64, 16))
-    ia, _ = O.topk_route(z, 4, O.TOPK_SOFTMAX)
-    ib, _ = O.topk_route(z, 4, O.SOFTMAX_TOPK)
+    ia, _ = impl.topk_route(z, 4, O.TOPK_SOFTMAX)
+    ib, _ = impl.topk_route(z, 4, O.SOFTMAX_TOPK)
     assert np.array_equal(ia, ib)
 
 
-def test_gate_weight_invariants_and_closed_forms():
+def test_gate_weight_invariants_and_closed_forms(impl):
     rng = np.random.default_rng(7)
     z = 3.0 * rng.standard_normal((50, 12))
     for k in (1, 2, 5, 12):
-        ia, wa = O.topk_route(z, k, O.TOPK_SOFTMAX)
-        ib, wb = O.topk_route(z, k, O.SOFTMAX_TOPK)
+        ia, wa = impl.topk_route(z, k, O.TOPK_SOFTMAX)
+        ib, wb = impl.topk_route(z, k, O.SOFTMAX_TOPK)
         assert np.allclose(wa.sum(axis=1), 1.0, atol=1e-12)
         assert (np.diff(wa, axis=1) <= 1e-15).all()           # best slot has the largest weight
         for t in range(z.shape[0]):
@@ -142,13 +155,13 @@ def test_gate_weight_invariants_and_closed_forms():
             assert np.allclose(wb.sum(axis=1), 1.0, atol=1e-12)
             assert np.allclose(wa, wb, atol=1e-14)               # k = N: the two modes coincide
     # k = 1 in mode A always gives weight exactly 1
-    _, w1 = O.topk_route(z, 1, O.TOPK_SOFTMAX)
+    _, w1 = impl.topk_route(z, 1, O.TOPK_SOFTMAX)
     assert (w1 == 1.0).all()
 
 
-def test_softmax_is_shift_invariant_and_stable_for_large_logits():
+def test_softmax_is_shift_invariant_and_stable_for_large_logits(impl):
     z = np.array([[1000.0, 999.0, -1000.0]])
-    _, w = O.topk_route(z, 2, O.TOPK_SOFTMAX)
+    _, w = impl.topk_route(z, 2, O.TOPK_SOFTMAX)
     e = math.exp(-1.0)
     assert np.allclose(w, [[1 / (1 + e), e / (1 + e)]], atol=1e-15, rtol=0)
 
@@ -162,31 +175,31 @@ def test_silu_closed_form_points():
 
 
 @pytest.mark.parametrize("ffn", [O.RELU2, O.SWIGLU])
-def test_expert_ffn_against_written_out_products(ffn):
+def test_expert_ffn_against_written_out_products(impl, ffn):
     rng = np.random.default_rng(8)
     M, d, d_ff = 3, 5, 7                      # non-square: a transposed operand cannot pass
     x = rng.standard_normal((M, d))
-    wg = rng.standard_normal((d_ff, d))
-    wu = rng.standard_normal((d_ff, d))
-    wd = rng.standard_normal((d, d_ff))
-    got = O.expert_ffn(x, wu, wd, ffn, wg if ffn == O.SWIGLU else None)
+    wg = rng.standard_normal((d, d_ff))
+    wu = rng.standard_normal((d, d_ff))
+    wd = rng.standard_normal((d_ff, d))
+    got = impl.expert_ffn(x, wu, wd, ffn, wg if ffn == O.SWIGLU else None)
     want = naive_ffn(x.tolist(), wu.tolist(), wd.tolist(), ffn, wg.tolist())
     assert got.shape == (M, d)
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
-def test_router_logits_against_written_out_product_and_bias():
+def test_router_logits_against_written_out_product_and_bias(impl):
     rng = np.random.default_rng(9)
     x = rng.standard_normal((4, 6))
-    wr = rng.standard_normal((3, 6))
-    b = np.array([0.5, -1.0, 2.0])
-    want = np.array(naive_matmul_t(x.tolist(), wr.tolist())) + b
-    assert np.allclose(O.router_logits(x, wr, b), want, rtol=1e-13, atol=1e-13)
+    wr = rng.standard_normal((6, 3))
+    b = np.array([0.5, -1.0, 2.0], dtype=np.float32)      # the bias is an fp32 input
+    want = np.array(naive_matmul(x.tolist(), wr.tolist())) + b.astype(np.float64)
+    assert np.allclose(impl.router_logits(x, wr, b), want, rtol=1e-13, atol=1e-13)
 
 
 # ---------------------------------------------------------------- whole-layer special cases
 @pytest.mark.parametrize("ffn", [O.RELU2, O.SWIGLU])
-def test_k_equals_n_is_dense_softmax_mixture(ffn):
+def test_k_equals_n_is_dense_softmax_mixture(impl, ffn):
     rng = np.random.default_rng(10)
     T, d, N, d_ff = 6, 4, 5, 3
     x, wr, wg, wu, wd = rand_layer(rng, T, d, N, d_ff, ffn)
@@ -199,12 +212,12 @@ def test_k_equals_n_is_dense_softmax_mixture(ffn):
         for e in range(N):
             want[t] += p[e] * expert_out[e][t]
     for gating in (O.TOPK_SOFTMAX, O.SOFTMAX_TOPK):
-        out = O.forward(x, wr, wu, wd, N, ffn, gating, w_gate=wg)
+        out = impl.forward(x, wr, wu, wd, N, ffn, gating, w_gate=wg)
         assert np.allclose(out["y"], want, rtol=1e-12, atol=1e-12)
 
 
 @pytest.mark.parametrize("ffn", [O.RELU2, O.SWIGLU])
-def test_identical_experts_reduce_to_one_ffn(ffn):
+def test_identical_experts_reduce_to_one_ffn(impl, ffn):
     rng = np.random.default_rng(11)
     T, d, N, d_ff, k = 7, 4, 6, 5, 3
     x, wr, wg, wu, wd = rand_layer(rng, T, d, N, d_ff, ffn)
@@ -213,22 +226,22 @@ def test_identical_experts_reduce_to_one_ffn(ffn):
     if wg is not None:
         wg[:] = wg[0]
     want = naive_ffn(x.tolist(), wu[0].tolist(), wd[0].tolist(), ffn, None if wg is None else wg[0].tolist())
-    out = O.forward(x, wr, wu, wd, k, ffn, O.TOPK_SOFTMAX, w_gate=wg)
+    out = impl.forward(x, wr, wu, wd, k, ffn, O.TOPK_SOFTMAX, w_gate=wg)
     assert np.allclose(out["y"], want, rtol=1e-12, atol=1e-12)
-    outb = O.forward(x, wr, wu, wd, k, ffn, O.SOFTMAX_TOPK, w_gate=wg)
+    outb = impl.forward(x, wr, wu, wd, k, ffn, O.SOFTMAX_TOPK, w_gate=wg)
     assert np.allclose(outb["y"], outb["w"].sum(axis=1, keepdims=True) * want, rtol=1e-12, atol=1e-12)
 
 
-def test_single_expert_is_plain_ffn():
+def test_single_expert_is_plain_ffn(impl):
     rng = np.random.default_rng(12)
     x, wr, wg, wu, wd = rand_layer(rng, 5, 4, 1, 6, O.SWIGLU)
-    out = O.forward(x, wr, wu, wd, 1, O.SWIGLU, O.TOPK_SOFTMAX, w_gate=wg)
+    out = impl.forward(x, wr, wu, wd, 1, O.SWIGLU, O.TOPK_SOFTMAX, w_gate=wg)
     want = naive_ffn(x.tolist(), wu[0].tolist(), wd[0].tolist(), O.SWIGLU, wg[0].tolist())
     assert np.allclose(out["y"], want, rtol=1e-12, atol=1e-12)
     assert out["counts"].tolist() == [5]
 
 
-def test_page_toy_layer_semantics():
+def test_page_toy_layer_semantics(impl):
     # The toy of page 2 (section 代码): experts are single d x d linears, top-k by
     # argsort, softmax over the picked logits, weighted sum of x @ W_e.  A ReLU
     # expert with W1 = I sees x > 0 unchanged, so it is the toy's linear expert.
@@ -243,40 +256,40 @@ def test_page_toy_layer_semantics():
         top = sorted(range(N), key=lambda e: gate[e])[-k:]
         w = naive_softmax([gate[e] for e in top])
         for wi, e in zip(w, top):
-            want[t] += wi * np.array(naive_matmul_t([x[t].tolist()], experts_W[e].T.tolist())[0])
-    out = O.forward(x, router_W.T, np.stack([np.eye(d)] * N), np.transpose(experts_W, (0, 2, 1)),
-                    k, O.RELU2, O.TOPK_SOFTMAX)
+            want[t] += wi * np.array(naive_matmul([x[t].tolist()], experts_W[e].tolist())[0])
+    # router_W and experts_W are taken as the toy lays them out (x @ W)
+    out = impl.forward(x, router_W, np.stack([np.eye(d)] * N), experts_W, k, O.RELU2, O.TOPK_SOFTMAX)
     assert np.allclose(out["y"], want, rtol=1e-11, atol=1e-12)
 
 
-def test_shared_expert_adds_plain_ffn_with_weight_one():
+def test_shared_expert_adds_plain_ffn_with_weight_one(impl):
     rng = np.random.default_rng(14)
     T, d, N, d_ff, k = 6, 4, 5, 3, 2
     x, wr, wg, wu, wd = rand_layer(rng, T, d, N, d_ff, O.SWIGLU)
-    sg, su, sd = rng.standard_normal((d_ff, d)), rng.standard_normal((d_ff, d)), rng.standard_normal((d, d_ff))
-    base = O.forward(x, wr, wu, wd, k, O.SWIGLU, O.SOFTMAX_TOPK, w_gate=wg)
-    with_sh = O.forward(x, wr, wu, wd, k, O.SWIGLU, O.SOFTMAX_TOPK, w_gate=wg, shared=(sg, su, sd))
+    sg, su, sd = rng.standard_normal((d, d_ff)), rng.standard_normal((d, d_ff)), rng.standard_normal((d_ff, d))
+    base = impl.forward(x, wr, wu, wd, k, O.SWIGLU, O.SOFTMAX_TOPK, w_gate=wg)
+    with_sh = impl.forward(x, wr, wu, wd, k, O.SWIGLU, O.SOFTMAX_TOPK, w_gate=wg, shared=(sg, su, sd))
     want_sh = naive_ffn(x.tolist(), su.tolist(), sd.tolist(), O.SWIGLU, sg.tolist())
     assert np.allclose(with_sh["y"] - base["y"], want_sh, rtol=1e-11, atol=1e-12)
     assert with_sh["counts"].sum() == T * k
 
 
-def test_token_subset_matches_full_evaluation():
+def test_token_subset_matches_full_evaluation(impl):
     rng = np.random.default_rng(15)
     x, wr, wg, wu, wd = rand_layer(rng, 20, 8, 6, 5, O.SWIGLU)
-    full = O.forward(x, wr, wu, wd, 2, O.SWIGLU, O.TOPK_SOFTMAX, w_gate=wg, capacity_factor=1.0)
-    sub = O.forward(x, wr, wu, wd, 2, O.SWIGLU, O.TOPK_SOFTMAX, w_gate=wg, capacity_factor=1.0,
+    full = impl.forward(x, wr, wu, wd, 2, O.SWIGLU, O.TOPK_SOFTMAX, w_gate=wg, capacity_factor=1.0)
+    sub = impl.forward(x, wr, wu, wd, 2, O.SWIGLU, O.TOPK_SOFTMAX, w_gate=wg, capacity_factor=1.0,
                     tokens=[19, 3, 7])
     assert np.allclose(sub["y"], full["y"][[19, 3, 7]], rtol=1e-13, atol=1e-14)
 
 
 # ---------------------------------------------------------------- grouping by expert
-def test_group_by_expert_invariants_and_brute_force():
+def test_group_by_expert_invariants_and_brute_force(impl):
     rng = np.random.default_rng(16)
     for trial in range(20):
         T, k, N = int(rng.integers(1, 40)), int(rng.integers(1, 4)), int(rng.integers(1, 9))
         idx = rng.integers(-1 if trial % 3 == 0 else 0, N, size=(T, k))
-        counts, offsets, perm, inv = O.group_by_expert(idx, N)
+        counts, offsets, perm, inv = impl.group_by_expert(idx, N)
         flat = idx.reshape(-1)
         kept = [s for s in range(T * k) if flat[s] >= 0]
         assert perm.tolist() == sorted(kept, key=lambda s: (flat[s], s))
@@ -295,21 +308,21 @@ def test_capacity_value_of_the_skewed_layer():
     assert O.expert_capacity(1.0, 10, 1, 3) == 4           # ceil(10/3)
 
 
-def test_capacity_64_reading():
+def test_capacity_64_reading(impl):
     # capacity 64: a token whose first choice already holds 63 slots still fits
     # (it becomes the 64th); the next one is re-routed to its next-best expert.
     T, N = 66, 4
     z = np.tile(np.array([3.0, 2.0, 1.0, 0.0]), (T, 1))
-    idx, w, fill = O.capacity_route(z, 1, 64)
+    idx, w, fill = impl.capacity_route(z, 1, 64)
     assert idx[:64, 0].tolist() == [0] * 64
     assert idx[64:, 0].tolist() == [1, 1]
     assert fill.tolist() == [64, 2, 0, 0]
     assert (w == 1.0).all()
 
 
-def test_capacity_drop_when_no_room_anywhere():
+def test_capacity_drop_when_no_room_anywhere(impl):
     z = np.array([[1.0, 0.0], [1.0, 0.0]])
-    idx, w, fill = O.capacity_route(z, 2, 1)
+    idx, w, fill = impl.capacity_route(z, 2, 1)
     assert idx.tolist() == [[0, -1], [1, -1]]
     assert w.tolist() == [[1.0, 0.0], [1.0, 0.0]]
     assert fill.tolist() == [1, 1]
@@ -338,7 +351,7 @@ def _replay_ok(z, idx, C):
     return True
 
 
-def test_capacity_serial_equals_independent_fixed_point():
+def test_capacity_serial_equals_independent_fixed_point(impl):
     rng = np.random.default_rng(17)
     for trial in range(60):
         T = int(rng.integers(1, 60))
@@ -348,7 +361,7 @@ def test_capacity_serial_equals_independent_fixed_point():
         z = rng.standard_normal((T, N)) - 2.0 * np.log(np.arange(N) + 1.0)[None, :]
         if trial % 4 == 0:
             z = np.round(z)                       # exact ties
-        idx, w, fill = O.capacity_route(z, k, C)
+        idx, w, fill = impl.capacity_route(z, k, C)
         idx2, fill2 = capacity_route_fixed_point(z, k, C)
         assert np.array_equal(idx, idx2), (trial, T, N, k, C)
         assert np.array_equal(fill, fill2)
@@ -361,13 +374,13 @@ def test_capacity_serial_equals_independent_fixed_point():
             assert np.allclose(w.sum(axis=1), 1.0, atol=1e-12)
 
 
-def test_capacity_large_enough_equals_plain_topk():
+def test_capacity_large_enough_equals_plain_topk(impl):
     rng = np.random.default_rng(18)
     z = rng.standard_normal((40, 6))
     for k in (1, 2, 3):
         C = O.expert_capacity(6 / k, 40, k, 6)          # cf = N/k -> C = T: never binds
-        idx, w, _ = O.capacity_route(z, k, C)
-        idx0, w0 = O.topk_route(z, k, O.TOPK_SOFTMAX)
+        idx, w, _ = impl.capacity_route(z, k, C)
+        idx0, w0 = impl.topk_route(z, k, O.TOPK_SOFTMAX)
         assert np.array_equal(idx, idx0)
         assert np.allclose(w, w0, atol=0, rtol=0)
 
@@ -583,10 +596,10 @@ def test_q4_quantize_bounds_and_grid():
     rng = np.random.default_rng(32)
     w = (rng.standard_normal((6, 256)) * 0.02).astype(np.float32)
     w[2, 128:] = 0.0                                   # an all-zero group
-    q, sc = O.quantize_q4(w)
+    q, sc = O.quantize_q4(w.T)                         # x W orientation: [K, rows]
     assert q.min() >= -7 and q.max() <= 7            # scale = amax / 7: the codes stay symmetric
     assert sc[2, 1] == 0 and np.all(q[2, 128:] == 0)
-    wh = O.dequantize_q4(q, sc)
+    wh = O.dequantize_q4(q, sc).T
     # round to nearest: each weight is within half a step of its code's value
     step = np.repeat(sc.astype(np.float64), 128, axis=1)
     assert np.all(np.abs(wh - w) <= 0.5 * step * (1 + 1e-6) + 1e-12)
@@ -601,13 +614,13 @@ def test_q4_quantize_bounds_and_grid():
     wg = np.tile(grid, 20)[:256].reshape(1, 256).astype(np.float32)
     wg[0, 0] = np.float32(0.875)                        # amax 7/8 in both groups -> scale 1/8
     wg[0, 128] = np.float32(-0.875)
-    q2, sc2 = O.quantize_q4(wg)
-    assert np.all(sc2 == np.float32(0.125)) and np.array_equal(O.dequantize_q4(q2, sc2), wg.astype(np.float64))
+    q2, sc2 = O.quantize_q4(wg.T)
+    assert np.all(sc2 == np.float32(0.125)) and np.array_equal(O.dequantize_q4(q2, sc2), wg.T.astype(np.float64))
 
 
 def test_q4_rounding_ties_to_even():
     # amax 7 -> scale exactly 1; w = 2.5 and -0.5 are ties: rint gives 2 and -0 (to even)
     w = np.zeros((1, 128), dtype=np.float32)
     w[0, :4] = [7.0, 2.5, -0.5, 3.5]
-    q, sc = O.quantize_q4(w)
+    q, sc = O.quantize_q4(w.T)
     assert sc[0, 0] == 1.0 and q[0, :4].tolist() == [7, 2, 0, 4]

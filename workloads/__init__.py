@@ -20,15 +20,15 @@ The skewed layer adds a fixed per-expert logit bias b[e] = -2 ln(e + 1)
 (a Zipf-like preference for low expert ids), computed in float64 and rounded
 to fp32 once, so both sides read the same fp32 values.
 
-Weight layout (the layout the C ABI takes, see include/moe.h): every weight is
-stored output-major, one row per output feature holding its input-side
-weights contiguously -- the layout of a linear layer's weight matrix:
+Weight layout (the layout the C ABI takes, see include/moe.h): the x W
+orientation of the configurations ("W_gate, W_up: d x d_ff; W_down: d_ff x d")
+and of the pages' toy (router_W [d, N], x @ experts_W[e]), row-major:
 
-  w_router [N, d]          z[t, e]   = sum_i x[t, i] * w_router[e, i]
-  w_gate   [N, d_ff, d]    g[t, f]   = sum_i x[t, i] * w_gate[e, f, i]
-  w_up     [N, d_ff, d]    u[t, f]   = sum_i x[t, i] * w_up[e, f, i]
-  w_down   [N, d, d_ff]    y[t, o]   = sum_f h[t, f] * w_down[e, o, f]
-  shared expert: sh_gate, sh_up [d_ff, d], sh_down [d, d_ff]
+  w_router [d, N]          z[t, e]   = sum_i x[t, i] * w_router[i, e]
+  w_gate   [N, d, d_ff]    g[t, f]   = sum_i x[t, i] * w_gate[e, i, f]
+  w_up     [N, d, d_ff]    u[t, f]   = sum_i x[t, i] * w_up[e, i, f]
+  w_down   [N, d_ff, d]    y[t, o]   = sum_f h[t, f] * w_down[e, f, o]
+  shared expert: sh_gate, sh_up [d, d_ff], sh_down [d_ff, d]
 
 For the two-layer ReLU expert, w_up holds W1 and w_down holds W2; w_gate is
 unused.
@@ -157,7 +157,7 @@ def make_inputs(cfg: LayerConfig, device="cpu", experts: Optional[range] = None)
     T, d, N, dff = cfg.T, cfg.d, cfg.N, cfg.d_ff
     out: Dict[str, Optional[torch.Tensor]] = {}
     out["x"] = _normal((T, d), 1.0, dt, device, _gen(device, cfg.seed, STREAM_X))
-    out["w_router"] = _normal((N, d), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_ROUTER))
+    out["w_router"] = _normal((d, N), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_ROUTER))
     out["logit_bias"] = zipf_bias(N).to(device) if cfg.zipf_bias else None
 
     def expert_stack(stream, rows, cols, std):
@@ -166,14 +166,14 @@ def make_inputs(cfg: LayerConfig, device="cpu", experts: Optional[range] = None)
             w[e].copy_(_normal((rows, cols), std, dt, device, _gen(device, cfg.seed, stream, e)))
         return w
 
-    out["w_gate"] = expert_stack(STREAM_GATE, dff, d, 1.0 / math.sqrt(d)) if cfg.ffn == FFN_SWIGLU else None
-    out["w_up"] = expert_stack(STREAM_UP, dff, d, 1.0 / math.sqrt(d))
-    out["w_down"] = expert_stack(STREAM_DOWN, d, dff, 1.0 / math.sqrt(dff))
+    out["w_gate"] = expert_stack(STREAM_GATE, d, dff, 1.0 / math.sqrt(d)) if cfg.ffn == FFN_SWIGLU else None
+    out["w_up"] = expert_stack(STREAM_UP, d, dff, 1.0 / math.sqrt(d))
+    out["w_down"] = expert_stack(STREAM_DOWN, dff, d, 1.0 / math.sqrt(dff))
     if cfg.has_shared:
-        out["sh_gate"] = (_normal((dff, d), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_SH_GATE))
+        out["sh_gate"] = (_normal((d, dff), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_SH_GATE))
                           if cfg.ffn == FFN_SWIGLU else None)
-        out["sh_up"] = _normal((dff, d), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_SH_UP))
-        out["sh_down"] = _normal((d, dff), 1.0 / math.sqrt(dff), dt, device, _gen(device, cfg.seed, STREAM_SH_DOWN))
+        out["sh_up"] = _normal((d, dff), 1.0 / math.sqrt(d), dt, device, _gen(device, cfg.seed, STREAM_SH_UP))
+        out["sh_down"] = _normal((dff, d), 1.0 / math.sqrt(dff), dt, device, _gen(device, cfg.seed, STREAM_SH_DOWN))
     else:
         out["sh_gate"] = out["sh_up"] = out["sh_down"] = None
     return out
@@ -183,7 +183,7 @@ def make_selection_router_inputs(cfg: LayerConfig, device="cpu", levels: int = 1
                                  grid_bias: bool = False) -> Dict[str, torch.Tensor]:
     """Inputs of one layer call whose router logits are exact in any summation order.
 
-    As make_inputs, except: row e of w_router is the unit vector on input feature e, so that
+    As make_inputs, except: column e of w_router is the unit vector on input feature e, so that
     logit z[t, e] is x[t, e] itself; x[t, :N] takes values k/8 for integer k drawn uniformly
     from [-levels/2, levels/2) (few distinct values: many exactly tied logits); with
     grid_bias, logit_bias[e] is a multiple of 1/4 in [-1, 1] (the sum with x stays exact in
@@ -195,7 +195,7 @@ def make_selection_router_inputs(cfg: LayerConfig, device="cpu", levels: int = 1
     g = _gen(device, cfg.seed, STREAM_GRID)
     steps = torch.randint(-(levels // 2), levels - levels // 2, (cfg.T, cfg.N), generator=g, device=device)
     out["x"][:, :cfg.N] = (steps.float() / 8.0).to(out["x"].dtype)
-    wr = torch.zeros((cfg.N, cfg.d), dtype=out["x"].dtype, device=device)
+    wr = torch.zeros((cfg.d, cfg.N), dtype=out["x"].dtype, device=device)
     wr[torch.arange(cfg.N, device=device), torch.arange(cfg.N, device=device)] = 1.0
     out["w_router"] = wr
     if grid_bias:
