@@ -184,6 +184,50 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str
     return "\n".join(lines) + "\n"
 
 
+def summarize_counters(pmc_dir: str, workload: str, command: str) -> str:
+    """Text summary of one rocprofv3 --pmc run: every counter's mean per dispatch for each kernel,
+    and for the MFMA kernels the matrix-core utilisation SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE x SIMDs), the shader clock GRBM_GUI_ACTIVE / duration, and the share of wave
+    cycles spent waiting (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES) and waiting on LDS."""
+    import csv
+    import glob
+    import statistics
+    vals = {}
+    durs = {}
+    for fn in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(fn)):
+            k = r["Kernel_Name"]
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for fn in glob.glob(os.path.join(pmc_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(fn)):
+            durs.setdefault(r["Kernel_Name"], []).append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    simds, xcds = 256 * 4, 8
+    lines = [f"# rocprofv3 counters per dispatch (mean over dispatches), {workload}",
+             f"# command: {command}",
+             "# Values are summed over the counter's instances (GRBM_GUI_ACTIVE over the 8 XCDs, so active cycles",
+             "# = GRBM_GUI_ACTIVE / 8).  mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (active cycles * 1024 SIMDs), as",
+             "# rocprofv3's MfmaUtil; clock = active cycles / kernel duration; wait = SQ_WAIT_INST_ANY /",
+             "# SQ_WAVE_CYCLES; lds_wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES"]
+    for k in sorted(vals, key=lambda k: -statistics.mean(durs.get(k, [0.0]))):
+        c = {n: statistics.mean(v) for n, v in vals[k].items()}
+        d = statistics.mean(durs[k]) if k in durs else float("nan")
+        lines.append(f"kernel {k[:110]}")
+        lines.append(f"  dispatches {len(next(iter(vals[k].values())))}, mean duration {d / 1e3:.1f} us")
+        for n in sorted(c):
+            lines.append(f"  {n} = {c[n]:.6g}")
+        g = c.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        if g and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            lines.append(f"  mfma_util = {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (g * simds):.4f}")
+        if g and d == d and d > 0:
+            lines.append(f"  clock_ghz = {g / d:.3f}")
+        if c.get("SQ_WAVE_CYCLES"):
+            if "SQ_WAIT_INST_ANY" in c:
+                lines.append(f"  wait = {c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.4f}")
+            if "SQ_WAIT_INST_LDS" in c:
+                lines.append(f"  lds_wait = {c['SQ_WAIT_INST_LDS'] / c['SQ_WAVE_CYCLES']:.4f}")
+    return "\n".join(lines) + "\n"
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -405,10 +449,16 @@ def main(argv=None) -> int:
                     help="first run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB", "COMMAND"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "COMMAND"),
+                    help="print the per-kernel counter summary of one rocprofv3 --pmc run and exit")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
         fd, wd, mib, cmd = args.summarize_pmc
         sys.stdout.write(summarize_pmc(fd, wd, int(mib) << 20, args.config, cmd))
+        return 0
+    if args.summarize_counters:
+        d, cmd = args.summarize_counters
+        sys.stdout.write(summarize_counters(d, args.config, cmd))
         return 0
     if args.gpus != 1:
         print(f"bench.py: the library runs one GPU's share of the layer; --gpus {args.gpus} is not "

@@ -56,25 +56,6 @@ struct FfnTile {
     static_assert(BM % ROWS_PER_PASS == 0 && BROWS % ROWS_PER_PASS == 0, "load passes");
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// LDS tile layout: rows of 64 bf16 (128 B, 8 chunks of 16 B), unpadded; chunk c of row r sits at
-// position c ^ ((r >> 1) & 7).  A fragment read serves 16 lanes (16 consecutive rows, one chunk,
-// 256 B) per LDS cycle; with this swizzle those 16 reads land in 16 distinct 16-byte bank groups
-// of the 64 banks.  One wave's direct global->LDS load (64 lanes x 16 B = 8 whole rows) stays
-// contiguous in LDS: lane l writes position l & 7 of row 8g + (l >> 3) and therefore fetches
-// chunk (l & 7) ^ ((4g + (l >> 4)) & 7) of that row.
-
-// 16 bytes per lane from base + voff + soff into LDS (M0 + 16 * lane): the buffer (MUBUF) form
-// of the direct load, with a raw-buffer descriptor (no range limit, 32-bit data format, the gfx9
-// encoding).  The per-lane offset is 32 bits and the K offset goes in a scalar register, so no
-// per-lane 64-bit address arithmetic is needed.  (A function of its own: the host pass drops a
-// kernel whose lambdas use the descriptor type.)
-__device__ __forceinline__ void buffer_load_lds16(const void* base, lds_void_t* dst, uint32_t voff, int soff) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
-}
-
 // Work split.  Wave 0 of every block turns offsets into a segment table in LDS: each segment's
 // first tile, its m-tile count (ceil(rows / BM)) and its row range.  Real tiles are numbered
 // segment by segment, K part outermost.  Within a segment they go in rectangles of at most 8
@@ -202,22 +183,6 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
     const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
     return (const char*)(((unsigned long long)hi << 32) | lo);
-}
-
-// Eight bf16 of one column and eight consecutive k-rows of a K-major LDS tile: two transposed
-// 8-byte reads (ds_read_b64_tr_b16), rows 0-3 at byte `off` of the LDS array `base` and rows 4-7
-// at off + second.  Within each group of 16 lanes, lane j receives element j & 3 of the 8 bytes
-// addressed by lane 4 e + (j >> 2), for e = 0..3: with lane L addressing row (L >> 2) at column
-// 4 (L & 3), lane j gets column j of the four rows.
-// The address is one offset from the array itself: the compiler then still knows which LDS
-// array each read touches, and need not wait for direct loads in flight into another one.
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-__device__ __forceinline__ bf16x8 lds_read_tr_b16x8(const void* base, int off, int second) {
-    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)((const char*)base + off));
-    const bf16x4_t hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)((const char*)base + (off + second)));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 struct TileInfo {

@@ -130,14 +130,24 @@ size_t ffn_ws_bytes(const moe_layer_desc& d) {
 char* at(void* ws, size_t off) { return (char*)ws + off; }
 
 // ---- stages (arguments already validated)
+// Steps 1-3.  z: where the logits go; want_z: whether anyone reads them afterwards (the caller, or
+// the capacity step) -- the fused router then writes them, and otherwise keeps them on chip.
 moe_status stage_route(const moe_layer_desc& d, const void* x, const void* wr, const float* bias, float* z,
-                       void* rpart, uint8_t* ranked, int32_t* idx, float* w, hipStream_t s,
+                       bool want_z, void* rpart, uint8_t* ranked, int32_t* idx, float* w, hipStream_t s,
                        hipEvent_t ev_mid) {
-    hipError_t e = launch_router_logits(x, wr, bias, z, rpart, d.T, d.d, d.N, d.dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "router logits launch");
-    if (!has_capacity(d)) {
-        e = launch_topk_gate(z, d.T, d.N, d.k, d.gating, idx, w, s);
-        if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    hipError_t e;
+    if (router_fused_supported(d.N, d.dtype)) {
+        const bool cap = has_capacity(d);
+        e = launch_router_topk(x, wr, bias, (want_z || cap) ? z : nullptr, d.T, d.d, d.N, d.k, d.gating,
+                               cap ? nullptr : idx, w, s);
+        if (e != hipSuccess) return hip_fail(e, "router launch");
+    } else {
+        e = launch_router_logits(x, wr, bias, z, rpart, d.T, d.d, d.N, d.dtype, s);
+        if (e != hipSuccess) return hip_fail(e, "router logits launch");
+        if (!has_capacity(d)) {
+            e = launch_topk_gate(z, d.T, d.N, d.k, d.gating, idx, w, s);
+            if (e != hipSuccess) return hip_fail(e, "top-k launch");
+        }
     }
     if (ev_mid) {
         e = hipEventRecord(ev_mid, s);
@@ -196,7 +206,8 @@ moe_status moe_route(const moe_layer_desc* desc, const void* x, const void* w_ro
     uint8_t* ranked = nullptr;
     if (has_capacity(d)) { ranked = (uint8_t*)at(ws, o); o += align256(capacity_workspace_bytes(d.T, d.N)); }
     void* rpart = router_workspace_bytes(d.T, d.d, d.N, d.dtype) ? at(ws, o) : nullptr;
-    return stage_route(d, x, w_router, logit_bias, z, rpart, ranked, idx, w, (hipStream_t)stream, nullptr);
+    return stage_route(d, x, w_router, logit_bias, z, logits != nullptr, rpart, ranked, idx, w, (hipStream_t)stream,
+                       nullptr);
 }
 
 moe_status moe_permute(const moe_layer_desc* desc, const int32_t* idx, int32_t* counts, int32_t* offsets,
@@ -282,8 +293,8 @@ moe_status forward_impl(const moe_layer_desc& d, const moe_weights& weights, con
 
     moe_status st;
     if ((st = record(ev(0), s)) != MOE_OK) return st;
-    st = stage_route(d, x, weights.w_router, weights.logit_bias, z, at(ws, L.h), (uint8_t*)at(ws, L.ranked),
-                     idx, w, s, ev(1));
+    st = stage_route(d, x, weights.w_router, weights.logit_bias, z, R.logits != nullptr, at(ws, L.h),
+                     (uint8_t*)at(ws, L.ranked), idx, w, s, ev(1));
     if (st != MOE_OK) return st;
     if ((st = record(ev(2), s)) != MOE_OK) return st;
     hipError_t e = launch_permute(idx, d.T, d.k, d.N, counts, offsets, perm, inv, s);

@@ -10,6 +10,11 @@ hipError_t launch_router_logits(const void* x, const void* wr, const float* bias
                                 int T, int d, int N, int dtype, hipStream_t s);
 hipError_t launch_topk_gate(const float* z, int T, int N, int k, int gating, int32_t* idx, float* w,
                             hipStream_t s);
+// Router GEMM fused with top-k and softmax (bf16, N in {64, 128, 256}): writes the logits to z
+// only if z is not null, and the routing (idx, w) only if idx is not null.
+bool router_fused_supported(int N, int dtype);
+hipError_t launch_router_topk(const void* x, const void* wr, const float* bias, float* z, int T, int d, int N,
+                              int k, int gating, int32_t* idx, float* w, hipStream_t s);
 // workspace of the capacity step: ranked lists [T, capacity_ranked_stride(N)] bytes, then [T]
 int capacity_ranked_stride(int N);
 size_t capacity_workspace_bytes(int T, int N);

@@ -190,20 +190,14 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(
 // ------------------------------------------------------------------ top-k + gate weights
 // One wave per token.  Each lane holds up to 4 logits (N <= 256) as 64-bit ranking keys
 // (descending logit, then ascending expert id).  k rounds of a wave-wide max pick the slots in
-// rank order.  Softmax in fp32 with the max subtracted.
-__global__ __launch_bounds__(256) void topk_gate_kernel(
-    const float* __restrict__ z, int T, int N, int k, int gating,
-    int32_t* __restrict__ idx, float* __restrict__ w) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= T) return;  // whole wave leaves together; no block barrier below
-    const float* zr = z + (size_t)t * N;
+// rank order.  Softmax in fp32 with the max subtracted.  zl[q] is the logit of expert lane + 64 q
+// (any value where that expert is past N).
+__device__ __forceinline__ void topk_gate_wave(const float (&zl)[4], int lane, int N, int k, int gating,
+                                               int32_t* __restrict__ idx_row, float* __restrict__ w_row) {
     uint64_t key[4];
-    float zl[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
-        zl[q] = e < N ? zr[e] : 0.f;
         key[q] = e < N ? rank_key(zl[q], e) : 0ull;
     }
     float zs[4] = {0.f, 0.f, 0.f, 0.f};  // the selected logits this lane records (slot j: lane j%64)
@@ -241,9 +235,207 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(
     for (int q = 0; q < 4; ++q) {
         const int j = lane + 64 * q;
         if (j < k) {
-            idx[(size_t)t * k + j] = es[q];
-            w[(size_t)t * k + j] = __expf(zs[q] - zmax) * inv;
+            idx_row[j] = es[q];
+            w_row[j] = __expf(zs[q] - zmax) * inv;
         }
+    }
+}
+
+__global__ __launch_bounds__(256) void topk_gate_kernel(
+    const float* __restrict__ z, int T, int N, int k, int gating,
+    int32_t* __restrict__ idx, float* __restrict__ w) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;  // whole wave leaves together; no block barrier below
+    const float* zr = z + (size_t)t * N;
+    float zl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        zl[q] = e < N ? zr[e] : 0.f;
+    }
+    topk_gate_wave(zl, lane, N, k, gating, idx + (size_t)t * k, w + (size_t)t * k);
+}
+
+// ------------------------------------------------------------------ router + top-k, fused
+// For bf16 layers with N = 64, 128 or 256 experts.  One block of 4 waves takes 32 tokens, every
+// expert and the whole K: per stage of 64 inputs the token tile (32 rows x 128 bytes) and the
+// router's weight tile (64 k-rows x N columns, K-major as stored) come into LDS by direct loads,
+// three stages in flight (three LDS arrays used in turn: the router's weight comes from L2 at
+// each block's own pace, so one stage ahead does not cover its latency),
+// and v_mfma_f32_16x16x32_bf16 multiplies them: token fragments by 16-byte reads (chunk c of row
+// r at c ^ ((r >> 1) & 7)), weight fragments by transposed reads (ds_read_b64_tr_b16; chunk c of
+// k-row r at c ^ f(r), f as in rf_woff, so that a read's 8 k-rows fall in distinct banks).  Wave w
+// owns expert tiles w, w + 4, ... of 16 experts and both 16-token row tiles.  The fp32 sums of
+// 256 inputs are added in fp64, as in the unfused router, and the bias is added in fp64 before
+// the one rounding to fp32.  The block's logits then go to LDS (and to memory if asked for), and
+// each wave ranks 8 of its tokens with the same top-k and softmax as the unfused kernel.
+#define RF_BT 32
+
+template <int NP>
+__device__ __forceinline__ int rf_woff(int r, int c) {     // byte of chunk c of k-row r
+    constexpr int ROWB = 2 * NP;
+    if (NP == 64) return r * ROWB + ((c ^ (2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)))) << 4);
+    return r * ROWB + ((c ^ (2 * ((r & 3) | (((r >> 3) & 1) << 2)))) << 4);
+}
+
+template <int NP>
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ wr, const float* __restrict__ bias,
+    float* __restrict__ z_out, int T, int d, int k, int gating, int do_topk, int32_t* __restrict__ idx,
+    float* __restrict__ w) {
+    static_assert(NP == 64 || NP == 128 || NP == 256, "weight tile swizzle for 64, 128 or 256 experts");
+    constexpr int ROWB = 2 * NP, WBYTES = 64 * ROWB, XBYTES = RF_BT * 128;
+    constexpr int SBYTES = XBYTES + WBYTES;
+    constexpr int NJ = NP / 64;                               // expert tiles per wave
+    constexpr int W_INS = WBYTES / 4096;                      // weight loads per wave per stage
+    constexpr int LPS = 1 + W_INS;                           // direct loads per wave per stage
+    static_assert(RF_BT * NP * 4 <= SBYTES, "the logit tile fits in one stage buffer");
+    static_assert(LPS <= 63, "vmcnt range");
+    // vmcnt(LPS) with lgkmcnt and expcnt left alone (gfx9 s_waitcnt encoding)
+    constexpr int WAIT_ONE_BEHIND = (LPS & 15) | ((LPS >> 4) << 14) | (7 << 4) | (15 << 8);
+    __shared__ __attribute__((aligned(1024))) char st0[SBYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[SBYTES];
+    __shared__ __attribute__((aligned(1024))) char st2[SBYTES];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t0 = blockIdx.x * RF_BT;
+    // direct-load offsets: token rows 8 wave .. 8 wave + 7 (rows past T load row t0), and this
+    // lane's weight chunks (the stage's first k-row goes in the scalar offset)
+    uint32_t xoff, woff[W_INS];
+    {
+        const int r = 8 * wave + (lane >> 3), pos = lane & 7;
+        const int t = t0 + r < T ? t0 + r : t0;
+        xoff = ((uint32_t)t * (uint32_t)d + (uint32_t)(8 * (pos ^ ((r >> 1) & 7)))) * 2u;
+#pragma unroll
+        for (int i = 0; i < W_INS; ++i) {
+            const int q = 1024 * (wave + 4 * i) + 16 * lane;
+            const int kr = q / ROWB, p = (q % ROWB) >> 4;
+            // chunk c sits at position p with rf_woff(kr, c) == q; the swizzle is an involution
+            const int c = (rf_woff<NP>(kr, p) - kr * ROWB) >> 4;
+            woff[i] = (uint32_t)(kr * NP + 8 * c) * 2u;
+        }
+    }
+    auto issue = [&](char* st, int k0) {
+        buffer_load_lds16(x, (lds_void_t*)(st + 1024 * wave), xoff, 2 * k0);
+#pragma unroll
+        for (int i = 0; i < W_INS; ++i)
+            buffer_load_lds16(wr, (lds_void_t*)(st + XBYTES + 1024 * (wave + 4 * i)), woff[i], 2 * k0 * NP);
+    };
+    // fragment offsets: token rows 16 rt + (lane & 15), chunk 4 ks + (lane >> 4); weight k-rows
+    // 32 ks + 8 (lane >> 4) + ((lane & 15) >> 2) (+4) of expert tile 4 j + wave
+    int aoff[2], boff[NJ];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int r = 16 * rt + (lane & 15);
+        aoff[rt] = r * 128 + ((((lane >> 4)) ^ ((r >> 1) & 7)) << 4);      // chunk (lane >> 4) of step 0
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int g = lane >> 4, L = lane & 15;
+        boff[j] = XBYTES + rf_woff<NP>(8 * g + (L >> 2), 2 * (4 * j + wave) + ((L & 3) >> 1)) + (L & 1) * 8;
+    }
+    f32x4 acc[2][NJ];
+    double acc64[2][NJ][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            acc[rt][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc64[rt][j][i] = 0.0;
+        }
+    auto fold = [&]() {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc64[rt][j][i] += (double)acc[rt][j][i];
+                acc[rt][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+    };
+    // two 32-input steps of one stage; step ks reads token chunks 4 ks + (lane >> 4), whose
+    // swizzled position is the step-0 one XOR 4 ks (the XOR term only touches bits 0-2)
+    auto compute = [&](const char* st) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 a[2], b[NJ];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) a[rt] = *(const bf16x8*)(st + (aoff[rt] ^ (ks << 6)));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) b[j] = lds_read_tr_b16x8(st, boff[j] + 32 * ks * ROWB, 4 * ROWB);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt], b[j], acc[rt][j], 0, 0, 0);
+        }
+    };
+    const int S = d / 64;                                     // stages (d % 64 == 0 for bf16)
+    // Stage s sits in array s % 3.  Before stage s is read, this wave's loads of stage s must have
+    // landed (the loads of stage s + 1, if issued, may still be in flight) and then every wave's
+    // (barrier); the barrier also ends every read of stage s - 1, whose array then takes stage s + 2.
+    // Every stage's loads go out unconditionally (past the last stage, that stage again, into an
+    // array no compute reads), so no wait depends on a branch: before stage s is read, this wave
+    // waits until at most one stage of its loads is in flight.  The barrier is s_barrier alone
+    // (after this wave's LDS reads have returned): __syncthreads() would also fence memory and so
+    // wait for every load in flight, stage s + 1's included.  The direct loads need no fence:
+    // their data is in LDS once the issuing wave's counter says so.
+    auto kst = [&](int i) { return 64 * (i < S ? i : S - 1); };
+    auto wait_stage = [&]() {
+        __builtin_amdgcn_s_waitcnt(WAIT_ONE_BEHIND);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    issue(st0, 0);
+    issue(st1, kst(1));
+    for (int s = 0; s < S; s += 3) {
+        wait_stage();
+        // (stage s + 2 goes out after this stage's reads: at the loop head the compiler no longer
+        // tells the arrays' loads apart and would wait for all of them before the first read)
+        compute(st0);
+        issue(st2, kst(s + 2));
+        if ((s + 1) % 4 == 0) fold();
+        if (s + 1 >= S) break;
+        wait_stage();
+        issue(st0, kst(s + 3));
+        compute(st1);
+        if ((s + 2) % 4 == 0) fold();
+        if (s + 2 >= S) break;
+        wait_stage();
+        issue(st1, kst(s + 4));
+        compute(st2);
+        if ((s + 3) % 4 == 0) fold();
+    }
+    if (S % 4 != 0) fold();                                   // a last, shorter chunk
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();                                          // every wave done with the stages
+    // logits: C layout of 16x16 MFMA, lane holds expert (lane & 15) of its tile, tokens
+    // 4 (lane >> 4) + i of its row tile
+    float* zt = (float*)st0;                                  // [RF_BT][NP]
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = 16 * (4 * j + wave) + (lane & 15);
+        const double b = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rt + 4 * (lane >> 4) + i;
+                const float zv = (float)(acc64[rt][j][i] + b);
+                zt[r * NP + e] = zv;
+                if (z_out && t0 + r < T) z_out[(size_t)(t0 + r) * NP + e] = zv;
+            }
+    }
+    if (!do_topk) return;
+    __syncthreads();
+    for (int rr = 0; rr < RF_BT / 4; ++rr) {
+        const int r = wave * (RF_BT / 4) + rr, t = t0 + r;
+        if (t >= T) break;                                    // uniform over the wave
+        float zl[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) zl[q] = (lane + 64 * q < NP) ? zt[r * NP + lane + 64 * q] : 0.f;
+        topk_gate_wave(zl, lane, NP, k, gating, idx + (size_t)t * k, w + (size_t)t * k);
     }
 }
 
@@ -549,6 +741,24 @@ hipError_t launch_router_logits(const void* x, const void* wr, const float* bias
         hipLaunchKernelGGL(router_logits_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                            s, (const float*)x, (const float*)wr, bias, z, T, d, N);
     }
+    return hipGetLastError();
+}
+
+bool router_fused_supported(int N, int dtype) { return dtype == 1 && (N == 64 || N == 128 || N == 256); }
+
+hipError_t launch_router_topk(const void* x, const void* wr, const float* bias, float* z, int T, int d, int N,
+                              int k, int gating, int32_t* idx, float* w, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid((unsigned)((T + RF_BT - 1) / RF_BT));
+    const int do_topk = idx != nullptr;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, bias, z, T, d, k, gating,
+                           do_topk, idx, w);
+    };
+    if (N == 64) go(router_topk_kernel<64>);
+    else if (N == 128) go(router_topk_kernel<128>);
+    else if (N == 256) go(router_topk_kernel<256>);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
