@@ -847,15 +847,23 @@ static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
 }
 
 // Decode-sized batches (at most 16 rows per expert on average) take the weight-streaming path.
-// Unroll depths and 16-column groups per wave (measured on the Mixtral decode layer): the
-// in-projection keeps one group and a shallow unroll, so that its registers stay low enough for
-// all of its waves to be resident at once (two groups: 0.38 vs 0.35 ms); the out-projection
-// takes two groups per wave, which halves its activation loads (0.17 vs 0.18 ms; four groups
-// leave too few waves for d = 4096).
+// 16-column groups per wave and unroll depths, measured on the Mixtral decode layer (one box,
+// 100 calls each): the in-projection takes four groups (whole 128-byte k-row pieces) two steps
+// at a time, 0.311 ms (four steps: 0.310; two groups: 0.407); the out-projection two groups four
+// steps at a time, 0.185 ms (eight steps: 0.195; four groups: 0.192; one group: 0.353).  Batches
+// double-buffered in registers were no faster (out-projection 0.190-0.201 ms).
+#ifndef SK_U_IN
 #define SK_U_IN 2
+#endif
+#ifndef SK_CG_IN
 #define SK_CG_IN 4
+#endif
+#ifndef SK_U_OUT
 #define SK_U_OUT 4
+#endif
+#ifndef SK_CG_OUT
 #define SK_CG_OUT 2
+#endif
 static bool skinny(const FfnLaunch& f) { return (long long)f.T * f.k <= 16LL * f.N; }
 
 // ------------------------------------------------------------------ fp32 path
