@@ -440,32 +440,59 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 }
 
 // ------------------------------------------------------------------ full ranking (capacity)
-// One token per 64-thread block: bitonic sort of the N ranking keys in LDS, descending.
+// One wave per token, four tokens per block: bitonic sort of the N ranking keys, descending, in
+// registers.  The P = max(64, N rounded up to a power of two) keys sit KPL = P / 64 to a lane,
+// element i in slot i % KPL of lane i / KPL; compare-exchanges at strides below KPL stay in a
+// lane, the others pair lanes by shuffles.  Keys past N are 0, below every real key (a real key's
+// upper half is the order-preserving map of its logit, never 0), so they sort last.
 // ranked[t * NP + r] = expert of rank r (uint8, N <= 256); rows are padded to NP = N rounded up
 // to 16 bytes with 0xFF, which is never a valid expert when padding exists (N < 256).
-__global__ __launch_bounds__(64) void rank_sort_kernel(const float* __restrict__ z, int T, int N, int NP,
-                                                       uint8_t* __restrict__ ranked) {
-    __shared__ uint64_t key[MOE_MAX_EXPERTS];
-    const int t = blockIdx.x, lane = threadIdx.x;
-    int P = 2;
-    while (P < N) P <<= 1;
+template <int KPL>
+__global__ __launch_bounds__(256) void rank_sort_kernel(const float* __restrict__ z, int T, int N, int NP,
+                                                        uint8_t* __restrict__ ranked) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    constexpr int P = 64 * KPL;
     const float* zr = z + (size_t)t * N;
-    for (int i = lane; i < P; i += 64) key[i] = i < N ? rank_key(zr[i], i) : 0ull;
-    __syncthreads();
+    uint64_t key[KPL];
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+        const int e = lane * KPL + s;
+        key[s] = e < N ? rank_key(zr[e], e) : 0ull;
+    }
+#pragma unroll
     for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int p = lane; p < (P >> 1); p += 64) {
-                const int i = 2 * stride * (p / stride) + (p % stride);
-                const int j = i + stride;
-                const uint64_t a = key[i], b = key[j];
-                const bool first_block = (i & size) == 0;
-                if (first_block ? (a < b) : (a > b)) { key[i] = b; key[j] = a; }
+            if (stride >= KPL) {                  // partner in lane ^ (stride / KPL), same slot
+#pragma unroll
+                for (int s = 0; s < KPL; ++s) {
+                    const int i = lane * KPL + s;
+                    const uint64_t o = shfl_xor_u64(key[s], stride / KPL);
+                    const bool keep_max = ((i & stride) == 0) == ((i & size) == 0);
+                    key[s] = keep_max ? (o > key[s] ? o : key[s]) : (o < key[s] ? o : key[s]);
+                }
+            } else {                              // partner in the same lane
+#pragma unroll
+                for (int s = 0; s < KPL; ++s) {
+                    if (s & stride) continue;
+                    const int i = lane * KPL + s;
+                    const uint64_t a = key[s], b = key[s + stride];
+                    const bool desc = (i & size) == 0;
+                    const bool sw = desc ? (a < b) : (a > b);
+                    key[s] = sw ? b : a;
+                    key[s + stride] = sw ? a : b;
+                }
             }
-            __syncthreads();
         }
     }
-    for (int r = lane; r < NP; r += 64)
-        ranked[(size_t)t * NP + r] = r < N ? (uint8_t)key_expert(key[r]) : (uint8_t)0xFF;
+    uint8_t* out = ranked + (size_t)t * NP;
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+        const int r = lane * KPL + s;
+        if (r < NP) out[r] = r < N ? (uint8_t)key_expert(key[s]) : (uint8_t)0xFF;
+    }
 }
 
 // ------------------------------------------------------------------ capacity routing
@@ -473,23 +500,36 @@ __global__ __launch_bounds__(64) void rank_sort_kernel(const float* __restrict__
 // all slot-1s, ...).  Within a pass, tokens are taken in chunks of CT (one per thread); a chunk
 // is resolved in parallel by deferred acceptance with token order as every expert's priority:
 // each token proposes to its best-ranked expert that it does not hold, that had room at the
-// start of the chunk and whose cut-off tau[e] is not below the token; an expert keeps its
-// (room)-th first proposers in token order and moves tau[e] to the last one kept.  tau only moves
-// down, so a token never returns to an expert that turned it away, and the fixed point is the
-// token-by-token first-come assignment.
+// start of the chunk and whose cut-off is not below the token; an expert keeps its (room)-th
+// first proposers in token order and moves its cut-off to the last one kept.  The cut-off only
+// moves down, so a token never returns to an expert that turned it away, and the fixed point is
+// the token-by-token first-come assignment.
 //
-// A 64-rank window of each chunk token's ranked list sits in LDS (4 ranks per dword,
-// rank-major, so a wave's lanes read neighbouring words), starting at the 16-rank boundary at
-// or before the rank the token resumes from; picks are shallow (on the skewed layer every pick
-// is within 41 ranks), and a scan that runs past the window reads the list from memory.  The
-// window keeps a chunk at one token per thread.  "Room at chunk start" is a byte table in LDS
-// and "already held" is in registers; a scan takes 16 ranks at a time, so a token steps over
-// full experts cheaply.  Proposal
-// counts are per wave, stamped with the round number, so no round has to clear them; after
-// round_limit rounds (at most 0xFFFF, the stamp's width) the counts are cleared and the stamps
-// start again at 1, at the top of a round, when no earlier round's count is read any more.
+// Both conditions sit in one LDS table of 16-bit chunk-local limits: lim[e] = -1 when e had no
+// room at the chunk's start, else the chunk index of the last token that may still propose to e
+// (CT - 1 until e is cut).  A scan takes 16 ranks at a time: the four words of the ranked row
+// and the 16 limits they name are read at once, and the candidate mask is built in registers,
+// so stepping over full or cut experts costs no dependent LDS read.
+//
+// The first 64 ranks of each chunk token's ranked list sit in LDS (4 ranks per dword,
+// rank-major, so a wave's lanes read neighbouring words); picks are shallow (on the skewed layer
+// every pick is within 41 ranks), and a scan that runs past them reads the list from memory.
+// The next chunk's ranks, held experts and resume rank are loaded while the current chunk runs;
+// none of these loads depends on another.  A wave loads the first 64 ranks of its own 64 tokens
+// four lanes to a row (16 rows per load), and scatters them into the rank-major layout at the
+// chunk's start (rows padded by 4 words, so that the four lanes writing one row hit four bank
+// groups).  The loads are unconditional (addresses clamped into the arrays), and a chunk's
+// picks are stored at the start of the next chunk of the same pass (a pass's last chunk stores
+// its own, before the next pass reads them): the vector memory counter counts stores too, so a
+// store issued just before the next chunk's loads are needed would make them wait for it.
+//
+// Proposal counts are per wave, stamped with the round number, so no round has to clear them;
+// after round_limit rounds (at most 0xFFFF, the stamp's width) the counts are cleared and the
+// stamps start again at 1, at the top of a round, when no earlier round's count is read any more.
+// Whether another round follows needs no block reduction: each wave's "a proposal was turned
+// away" flag is written after the round's first barrier and read after its second.
 #define CAP_THREADS 1024
-#define CAP_WIN 4                   // 16-byte pieces (16 ranks each) in a token's window
+#define CAP_WIN 4                   // 16-byte pieces (16 ranks each) of a token's list in LDS
 
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void capacity_kernel(
@@ -498,41 +538,45 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
     constexpr int CAP_THREADS_ = THREADS;
     constexpr int CAP_WAVES_ = THREADS / 64;
     constexpr int WW = 4 * CAP_WIN;                     // window words
-    __shared__ uint32_t rk4[WW * THREADS];              // [WW][CT]
+    static_assert(CAP_WAVES_ % 4 == 0, "wave flags are read four at a time");
+    __shared__ uint32_t rk4[WW * (THREADS + 4)];        // [WW][CT + 4]
     __shared__ uint32_t cnt[CAP_WAVES_][MOE_MAX_EXPERTS]; // (round << 16) | proposals of the wave
     __shared__ int fill[MOE_MAX_EXPERTS];
-    __shared__ int tau[MOE_MAX_EXPERTS];
-    __shared__ uint8_t roomb[MOE_MAX_EXPERTS];          // 1: expert had room at chunk start
+    __shared__ int16_t lim[MOE_MAX_EXPERTS];            // chunk-local cut-off, -1: full at chunk start
+    __shared__ u32x4 rejw[CAP_WAVES_ / 4];              // per wave: a proposal was turned away
     const int tid = threadIdx.x, lane = tid & 63;
-    (void)lane;
     const int wave = tid >> 6;
     const int NQ = NP >> 2;               // words per ranked row (multiple of 4)
+    const int NPC = NQ >> 2;              // 16-rank pieces per ranked row
     for (int e = tid; e < MOE_MAX_EXPERTS; e += CAP_THREADS_) fill[e] = 0;
     for (int i = tid; i < CAP_WAVES_ * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&cnt[0][0])[i] = 0u;
     uint32_t round = 0;                   // stamp of the current round's counts, 1 .. round_limit
 
-    // next chunk's state of this thread's token, fetched during the current chunk: the window
-    // of its ranked row, the first four experts it already holds and the rank after its
-    // previous slot's pick
-    u32x4 pre[CAP_WIN];
-    int ph0 = -1, ph1 = -1, ph2 = -1, ph3 = -1, pstart = 0, pq0 = 0;
-    auto prefetch = [&](int t_next, int j_next) {
-        if (tid >= CT || t_next >= T) return;
+    // next chunk's state, fetched during the current chunk: for this thread's token the first
+    // four experts it already holds and the rank after its previous slot's pick; for the wave's
+    // 64 tokens the first CAP_WIN pieces of their ranked rows, piece (lane & 3) of row
+    // 16 i + (lane >> 2) in pre[i] (CAP_WIN == 4: every piece of the window once)
+    static_assert(CAP_WIN == 4, "one 16-byte piece per lane and load");
+    u32x4 pre[4];
+    int ph0 = -1, ph1 = -1, ph2 = -1, ph3 = -1, pstart = 0;
+    const int wrow0 = 64 * wave;                         // the wave's first token in a chunk
+    const int pc = lane & 3;                             // piece of a row this lane carries
+    auto prefetch = [&](int c_next) {                   // c_next: first token of the next chunk
+        const int t_next = min(c_next + tid, T - 1);     // rows past T: loaded, never used
         const int32_t* ir = idx + (size_t)t_next * k;
-        ph0 = j_next > 0 ? ir[0] : -1;
-        ph1 = j_next > 1 ? ir[1] : -1;
-        ph2 = j_next > 2 ? ir[2] : -1;
-        ph3 = j_next > 3 ? ir[3] : -1;
-        pstart = j_next > 0 ? rpos[t_next] : 0;
-        pq0 = (pstart >> 4) << 2;                           // window start (words), 16-rank aligned
-        const u32x4* row = (const u32x4*)(ranked + (size_t)t_next * NP) + (pq0 >> 2);
-        const int npieces = (NQ - pq0) >> 2;                // pieces left in the row
+        if (k > 1) { ph0 = ir[0]; pstart = rpos[t_next]; }      // only what a later pass reads
+        if (k > 2) ph1 = ir[1];
+        if (k > 3) ph2 = ir[2];
+        if (k > 4) ph3 = ir[3];                          // masked by the pass where used
 #pragma unroll
-        for (int i = 0; i < CAP_WIN; ++i)
-            if (i < npieces) pre[i] = row[i];
+        for (int i = 0; i < 4; ++i) {
+            const int r = min(c_next + wrow0 + 16 * i + (lane >> 2), T - 1);
+            pre[i] = *((const u32x4*)(ranked + (size_t)r * NP) + min(pc, NPC - 1));
+        }
     };
     const int nchunks = (T + CT - 1) / CT;
-    prefetch(tid, 0);
+    int pend_t = -1, pend_choice = -1, pend_rpos = 0;  // pick not stored yet (same pass)
+    prefetch(0);
     __syncthreads();
 
     for (int j = 0; j < k; ++j) {
@@ -540,30 +584,31 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
             const int c0 = ci * CT;
             const int t = c0 + tid;
             const bool active = tid < CT && t < T;
-            const int wq0 = pq0;                            // this chunk token's window start
-            if (active) {
-                const int npieces = (NQ - wq0) >> 2;
+            // every lane writes (rows past T and pieces past the row hold junk that no scan
+            // reads), so that every load of the prefetch is waited for on every path
 #pragma unroll
-                for (int i = 0; i < CAP_WIN; ++i)
-                    if (i < npieces) {
-                        rk4[(4 * i + 0) * CT + tid] = pre[i][0];
-                        rk4[(4 * i + 1) * CT + tid] = pre[i][1];
-                        rk4[(4 * i + 2) * CT + tid] = pre[i][2];
-                        rk4[(4 * i + 3) * CT + tid] = pre[i][3];
-                    }
+            for (int i = 0; i < 4; ++i) {
+                const int r = wrow0 + 16 * i + (lane >> 2);
+                rk4[(4 * pc + 0) * (CT + 4) + r] = pre[i][0];
+                rk4[(4 * pc + 1) * (CT + 4) + r] = pre[i][1];
+                rk4[(4 * pc + 2) * (CT + 4) + r] = pre[i][2];
+                rk4[(4 * pc + 3) * (CT + 4) + r] = pre[i][3];
             }
-            const int h0 = ph0, h1 = ph1, h2 = ph2, h3 = ph3;
+            if (pend_t >= 0) {                             // the previous chunk's pick
+                idx[(size_t)pend_t * k + j] = pend_choice;
+                rpos[pend_t] = (uint8_t)pend_rpos;
+                pend_t = -1;
+            }
+            const int h0 = j > 0 ? ph0 : -1, h1 = j > 1 ? ph1 : -1, h2 = j > 2 ? ph2 : -1, h3 = j > 3 ? ph3 : -1;
             // the rank after the previous slot's pick: everything ranked above it was held or
             // full then, and fills never go down
-            const int start = pstart;
-            for (int e = tid; e < MOE_MAX_EXPERTS; e += CAP_THREADS_) {
-                tau[e] = 0x7FFFFFFF;
-                roomb[e] = (e < N && fill[e] < C) ? 1 : 0;
-            }
+            const int start = j > 0 ? pstart : 0;
+            for (int e = tid; e < MOE_MAX_EXPERTS; e += CAP_THREADS_)
+                lim[e] = (int16_t)((e < N && fill[e] < C) ? CT - 1 : -1);
             __syncthreads();
             // next: the following chunk of this pass (the first chunk of the next pass is fetched
             // once this chunk's picks are written: with a single chunk they are its own tokens)
-            if (ci + 1 < nchunks) prefetch(t + CT, j);
+            if (ci + 1 < nchunks) prefetch(c0 + CT);
             int q = start >> 2, bpos = start & 3, choice = -1;
             bool choose = active;
             while (true) {
@@ -577,18 +622,16 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                 ++round;
                 if (choose) {                             // next candidate from (q, bpos) on
                     choice = -1;
-                    // one aligned piece of four words (16 ranks) at a time: the words, then the
-                    // room flags of their 16 experts, each read at once, so a scan over full
-                    // experts waits for two LDS reads per 16 ranks
+                    // one aligned piece of four words (16 ranks): the limits of its 16 experts,
+                    // all read at once (any byte indexes the table; words past the row's end are
+                    // masked afterwards), give the candidates; then only the held check is left
                     auto piece = [&](const uint32_t (&wd)[4], int q0) {
-                        // all 16 reads unconditional (any byte indexes the table), so that they go
-                        // out together; words past the row's end are masked afterwards
-                        uint32_t rf = 0;                    // bit 4 i + b: word i, byte b had room
+                        uint32_t rf = 0;                    // bit 4 i + b: word i, byte b may be proposed to
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
 #pragma unroll
                             for (int b = 0; b < 4; ++b)
-                                rf |= (uint32_t)roomb[(wd[i] >> (8 * b)) & 0xFF] << (4 * i + b);
+                                rf |= (uint32_t)(tid <= (int)lim[(wd[i] >> (8 * b)) & 0xFF]) << (4 * i + b);
                         if (NQ - q0 < 4) rf &= (1u << (4 * (NQ - q0))) - 1u;
                         rf &= ~0u << (4 * (q - q0) + bpos);    // ranks before the resume point
                         while (rf) {
@@ -597,7 +640,6 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                             const uint32_t w = (p >> 2) == 0 ? wd[0] : (p >> 2) == 1 ? wd[1]
                                              : (p >> 2) == 2 ? wd[2] : wd[3];
                             const int e = (w >> (8 * (p & 3))) & 0xFF;
-                            if (t > tau[e]) continue;                         // turned away this chunk
                             bool held = e == h0 || e == h1 || e == h2 || e == h3;
                             for (int jj = 4; jj < j && !held; ++jj) held = idx[(size_t)t * k + jj] == e;
                             if (held) continue;
@@ -610,16 +652,15 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                         bpos = 0;
                         return false;
                     };
-                    // inside the window (it starts on a piece boundary): LDS reads only, so no
-                    // wait for the next chunk's loads still in flight
-                    while (q < NQ && (q & ~3) - wq0 < WW) {
+                    // the first WW words from LDS: no wait for the next chunk's loads in flight
+                    while (q < NQ && q < WW) {
                         const int q0 = q & ~3;
                         uint32_t wd[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) wd[i] = rk4[(q0 + i - wq0) * CT + tid];   // in the window array
+                        for (int i = 0; i < 4; ++i) wd[i] = rk4[(q0 + i) * (CT + 4) + tid];
                         if (piece(wd, q0)) break;
                     }
-                    // past the window (rare): the rest of the ranked row from memory
+                    // past them (rare): the rest of the ranked row from memory
                     while (choice < 0 && q < NQ) {
                         const int q0 = q & ~3;
                         uint32_t wd[4];
@@ -648,20 +689,36 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                     for (int ww = 0; ww < CAP_WAVES_; ++ww)
                         rank += (ww < wave && (cw[ww] >> 16) == round) ? (int)(cw[ww] & 0xFFFF) : 0;
                     const int room = C - fill[choice];
-                    if (rank == room - 1) tau[choice] = t;
+                    if (rank == room - 1) lim[choice] = (int16_t)tid;
                     if (rank >= room) {
                         rejected = true;
                         if (++bpos == 4) { bpos = 0; ++q; }
                         choose = true;
                     }
                 }
-                if (!__syncthreads_or(rejected)) break;
+                // another round if any wave turned a proposal away: one flag per wave, written
+                // after this round's first barrier (every wave has read the previous round's
+                // flags by then) and read after the second
+                const bool wrej = __ballot(rejected) != 0ull;
+                if (lane == 0) ((uint32_t*)rejw)[wave] = wrej ? 1u : 0u;
+                __syncthreads();
+                u32x4 any = rejw[0];
+#pragma unroll
+                for (int i = 1; i < CAP_WAVES_ / 4; ++i) any |= rejw[i];
+                if ((any[0] | any[1] | any[2] | any[3]) == 0u) break;
             }
             if (active) {
-                idx[(size_t)t * k + j] = choice;
-                rpos[t] = (uint8_t)(choice >= 0 ? (q * 4 + bpos + 1 < 256 ? q * 4 + bpos + 1 : 255) : 255);
+                const int rp = choice >= 0 ? (q * 4 + bpos + 1 < 256 ? q * 4 + bpos + 1 : 255) : 255;
+                if (ci + 1 == nchunks) {
+                    idx[(size_t)t * k + j] = choice;
+                    rpos[t] = (uint8_t)rp;
+                } else {
+                    pend_t = t;
+                    pend_choice = choice;
+                    pend_rpos = rp;
+                }
             }
-            if (ci + 1 == nchunks && j + 1 < k) prefetch(tid, j + 1);
+            if (ci + 1 == nchunks && j + 1 < k) prefetch(0);
             if (tid < N) {                                // at the fixed point every proposal is kept
                 int s = 0;
                 for (int ww = 0; ww < CAP_WAVES_; ++ww) {
@@ -786,7 +843,10 @@ hipError_t launch_capacity(const float* z, uint8_t* ranked, int T, int N, int k,
                            int32_t* idx, float* w, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int NP = capacity_ranked_stride(N);
-    hipLaunchKernelGGL(rank_sort_kernel, dim3(T), dim3(64), 0, s, z, T, N, NP, ranked);
+    const dim3 sgrid((unsigned)((T + 3) / 4));
+    if (N <= 64) hipLaunchKernelGGL(rank_sort_kernel<1>, sgrid, dim3(256), 0, s, z, T, N, NP, ranked);
+    else if (N <= 128) hipLaunchKernelGGL(rank_sort_kernel<2>, sgrid, dim3(256), 0, s, z, T, N, NP, ranked);
+    else hipLaunchKernelGGL(rank_sort_kernel<4>, sgrid, dim3(256), 0, s, z, T, N, NP, ranked);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // one token per thread and chunk (the ranked-list windows of 1024 tokens take 64 KiB of LDS)
