@@ -696,11 +696,10 @@ struct SkinnyTile {
 };
 
 // Weight loads are non-temporal when a wave's k-row piece is a whole 128-byte line (four
-// 16-column groups): each weight byte is read once per call, and the gate/up stream of the
-// Mixtral decode layer then runs at 6.7 TB/s (0.281 vs 0.312 ms).  With two groups per wave the
-// neighbouring wave reads the other half of each line, which the L2 then no longer holds
-// (down projection 0.234 vs 0.185 ms); with four groups the down projection gains nothing
-// (0.186 ms), so it keeps two.
+// 16-column groups): each weight byte is read once per call, and both streams of the Mixtral
+// decode layer then run at 6.7 TB/s (gate/up 0.281 vs 0.312 ms with ordinary loads).  With two
+// groups per wave the neighbouring wave reads the other half of each line, which the L2 then
+// no longer holds (down projection 0.234 vs 0.185 ms).
 #ifndef SK_NT_MIN_CG
 #define SK_NT_MIN_CG 4
 #endif
@@ -713,7 +712,10 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
     const int gw = blockIdx.x * 4 + wv;                        // global wave id
     const int ngroups = (a.Ncols + 16 * CG - 1) / (16 * CG);
     const int nseg = a.N + (a.has_shared ? 1 : 0);
-    const int seg = gw / ngroups, cg = gw % ngroups;
+    // K parts (out-projection): part kp of a segment takes K steps [kp KS, (kp + 1) KS) and
+    // writes its partial sums to part kp of the output, which the combine adds in order
+    const int nkp = (MODE == MODE_OUT && a.ksplit > 1) ? a.ksplit : 1;
+    const int seg = gw / (ngroups * nkp), kp = (gw / ngroups) % nkp, cg = gw % ngroups;
     if (seg >= nseg) return;                                   // no block barrier below
     int row_beg, row_end;
     const bf16 *B0, *B1 = nullptr;
@@ -730,8 +732,10 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
         if (NB == 2) B1 = a.S1;
     }
     if (row_end <= row_beg) return;                             // expert not touched
-    const int KS = a.K / 32;
+    const int KS = a.K / 32 / nkp;                              // K steps of this wave
     const size_t step = (size_t)32 * a.Ncols;                   // elements between K steps
+    B0 += (size_t)kp * KS * step;
+    if (NB == 2) B1 += (size_t)kp * KS * step;
     // this lane's weight loads (CG per matrix and step): k-row q RPI + lane / CPR, chunk lane % CPR
     // of the wave's columns (Ncols is a multiple of 64, so every column group is whole); where they
     // go in the tile; and where its transposed reads start
@@ -760,7 +764,7 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
         int src;
         if (MODE == MODE_OUT) src = rok ? r : m0;
         else src = (seg < a.N) ? a.perm[rok ? r : m0] / a.k : (rok ? r : m0) - a.T * a.k;
-        const bf16* pa = a.A + (size_t)src * a.K + kq;
+        const bf16* pa = a.A + (size_t)src * a.K + kq + kp * KS * 32;
         f32x4 acc0[CG], acc1[CG];
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
@@ -840,7 +844,7 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
                 if (row >= row_end) continue;
                 if (MODE == MODE_OUT) {
                     const float scale = (a.row_scale && seg < a.N) ? a.row_scale[a.perm[row]] : 1.0f;
-                    ((float*)a.C)[(size_t)row * a.Ncols + col] = acc0[c][i] * scale;
+                    ((float*)a.C)[kp * a.part_stride + (size_t)row * a.Ncols + col] = acc0[c][i] * scale;
                 } else if (MODE == MODE_IN_SWIGLU) {
                     ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)(silu_f32(acc0[c][i]) * acc1[c][i]);
                 } else {
@@ -853,7 +857,8 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
 
 template <int MODE, int U, int CG>
 static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
-    const long long waves = (long long)(a.N + (a.has_shared ? 1 : 0)) * ((a.Ncols + 16 * CG - 1) / (16 * CG));
+    const int nkp = (MODE == MODE_OUT && a.ksplit > 1) ? a.ksplit : 1;
+    const long long waves = (long long)(a.N + (a.has_shared ? 1 : 0)) * ((a.Ncols + 16 * CG - 1) / (16 * CG)) * nkp;
     auto kern = ffn_skinny_kernel<MODE, U, CG>;
     hipLaunchKernelGGL(kern, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
@@ -861,10 +866,12 @@ static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
 
 // Decode-sized batches (at most 16 rows per expert on average) take the weight-streaming path.
 // 16-column groups per wave and unroll depths, measured on the Mixtral decode layer (one box,
-// 100 calls each): the in-projection takes four groups (whole 128-byte k-row pieces) two steps
-// at a time, 0.311 ms (four steps: 0.310; two groups: 0.407); the out-projection two groups four
-// steps at a time, 0.185 ms (eight steps: 0.195; four groups: 0.192; one group: 0.353).  Batches
-// double-buffered in registers were no faster (out-projection 0.190-0.201 ms).
+// 200 calls each): the in-projection takes four groups (whole 128-byte k-row pieces) two steps
+// at a time, 0.281 ms with non-temporal loads (four steps: 0.280; two groups: 0.407).  The
+// out-projection takes four groups two steps at a time, in two K parts (so that its
+// 8 x 64 column groups still give every SIMD a wave): 0.141 ms, against 0.185 ms with two
+// groups, four steps and one part, 0.186 ms with four groups in one part, and 0.193 ms with
+// two groups in two parts.  Batches double-buffered in registers were no faster.
 #ifndef SK_U_IN
 #define SK_U_IN 2
 #endif
@@ -872,10 +879,10 @@ static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
 #define SK_CG_IN 4
 #endif
 #ifndef SK_U_OUT
-#define SK_U_OUT 4
+#define SK_U_OUT 2
 #endif
 #ifndef SK_CG_OUT
-#define SK_CG_OUT 2
+#define SK_CG_OUT 4
 #endif
 static bool skinny(const FfnLaunch& f) { return (long long)f.T * f.k <= 16LL * f.N; }
 
@@ -999,13 +1006,18 @@ static bool tiles_320_out(const FfnLaunch& f) {
     return rows >= 240LL * f.N && rows <= 288LL * f.N;
 }
 
-// K parts for the out-projection: two when its K is long and one part alone would leave the
-// last round of blocks on the CUs mostly empty.  The parts' fp32 outputs are summed, in order,
+// K parts for the out-projection: for the tiled GEMM two when its K is long and one part alone
+// would leave the last round of blocks on the CUs mostly empty; for the weight stream two when
+// one part would run at most one wave per SIMD.  The parts' fp32 outputs are summed, in order,
 // by the combine.
 int ffn_out_ksplit(int T, int k, int N, int d, int d_ff, int has_shared, int dtype) {
     if (dtype != 1) return 1;
     const long long rows = (long long)T * k;
-    if (rows <= 16LL * N) return 1;                        // weight streaming (decode)
+    if (rows <= 16LL * N) {                                // weight streaming (decode)
+        // two parts when one would give the stream at most one wave per SIMD
+        const long long waves = (long long)(N + (has_shared ? 1 : 0)) * ((d + 16 * SK_CG_OUT - 1) / (16 * SK_CG_OUT));
+        return (waves <= 1024 && (d_ff / 32) % 2 == 0) ? 2 : 1;
+    }
     if (d_ff % (2 * FB_BK) != 0 || d_ff < 8192) return 1;
     if (rows < 192LL * N) return 1;                       // small-tile path: many blocks already
     const long long tiles = ((rows + 255) / 256 + N + (has_shared ? (T + 255) / 256 : 0)) * ((d + 255) / 256);
