@@ -511,7 +511,7 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         # samples sized for roughly 10-20 s of oracle work each, on 16 host cores and on one
-        default_sample = {"tiny_fp32": 128, "mixtral_prefill": 256, "mixtral_decode": 16,
+        default_sample = {"tiny_fp32": 128, "mixtral_prefill": 768, "mixtral_decode": 16,
                           "deepseek_v3": 256, "skewed_capacity": 2048}.get(cfg.name, 64)
         S = args.cpu_sample_tokens or default_sample
         out["cpu_baseline"] = cpu_baseline(cfg, inp, S, max(1, S // 16))
