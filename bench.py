@@ -228,6 +228,21 @@ def summarize_counters(pmc_dir: str, workload: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def summarize_stats(stats_csv: str, workload: str, command: str, note: str = "") -> str:
+    """Text table of a rocprofv3 --kernel-trace --stats run (its kernel_stats.csv): calls, mean,
+    min and max duration and share of the total per kernel, longest total first."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics, {workload}", f"# command: {command}"]
+    if note:
+        lines.append(f"# {note}")
+    lines.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")
+    for r in rows:
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} {float(r['MinNs']) / 1e3:10.1f} "
+                     f"{float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}  {r['Name'][:100]}")
+    return "\n".join(lines) + "\n"
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -451,6 +466,8 @@ def main(argv=None) -> int:
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "COMMAND"),
                     help="print the per-kernel counter summary of one rocprofv3 --pmc run and exit")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "COMMAND", "NOTE"),
+                    help="print the kernel table of one rocprofv3 --kernel-trace --stats run and exit")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
         fd, wd, mib, cmd = args.summarize_pmc
@@ -459,6 +476,10 @@ def main(argv=None) -> int:
     if args.summarize_counters:
         d, cmd = args.summarize_counters
         sys.stdout.write(summarize_counters(d, args.config, cmd))
+        return 0
+    if args.summarize_stats:
+        f, cmd, note = args.summarize_stats
+        sys.stdout.write(summarize_stats(f, args.config, cmd, note))
         return 0
     if args.gpus != 1:
         print(f"bench.py: the library runs one GPU's share of the layer; --gpus {args.gpus} is not "
