@@ -82,14 +82,19 @@ __device__ __forceinline__ int variant_nv(int nsub) {
 }
 
 // Estimated cost of a tile in 1/256 of a full tile: a short tile (an expert's last m-tile) runs
-// the variant with fewer sub-tiles per wave and costs about half a full tile plus its share of
-// the MFMAs (measured: a 64-row tile of 256 takes 0.65 of a full one).
-template <int TM, int WGM>
-__device__ __forceinline__ int tile_cost(int rows_in_tile) {
-    return 128 + 128 * variant_nv<TM, WGM>((rows_in_tile + 31) / 32) / TM;
+// the variant with fewer sub-tiles per wave and costs a fixed part, its weight stream, plus its
+// share of the MFMAs.  The fixed part is half a tile (measured: a 64-row tile of 256 takes 0.65
+// of a full one), except for a 320-row in-projection tile that is its expert's only one: no
+// other m-tile shares its weight tiles through the L2, and it counts 160/256 (fitted to the
+// XCDs' finishing times on the skewed layer, where such tiles of 64 rows took 0.69 of a full one
+// and the two XCDs holding them finished 15% after the rest with the half-tile estimate).
+template <int MODE, int TM, int WGM>
+__device__ __forceinline__ int tile_cost(int rows_in_tile, bool alone) {
+    const int fix = (MODE != MODE_OUT && TM >= 5 && alone) ? 160 : 128;
+    return fix + (256 - fix) * variant_nv<TM, WGM>((rows_in_tile + 31) / 32) / TM;
 }
 
-template <int BM, int TM, int WGM>
+template <int MODE, int BM, int TM, int WGM>
 __device__ __forceinline__ void build_segments(const FfnKArgs& a, int lane, int* s_tab, int* s_R1, int* s_C1) {
     int tl[5], beg[5], rows[5], cost[5], loc = 0, cloc = 0;
 #pragma unroll
@@ -106,7 +111,7 @@ __device__ __forceinline__ void build_segments(const FfnKArgs& a, int lane, int*
         }
         tl[q] = (rows[q] + BM - 1) / BM;
         const int part = rows[q] % BM;
-        cost[q] = a.n_tiles * ((rows[q] / BM) * 256 + (part ? tile_cost<TM, WGM>(part) : 0));
+        cost[q] = a.n_tiles * ((rows[q] / BM) * 256 + (part ? tile_cost<MODE, TM, WGM>(part, rows[q] < BM) : 0));
         loc += tl[q];
         cloc += cost[q];
     }
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go to M0
     static_assert(FFN_MAX_SEG > MOE_MAX_EXPERTS + 1, "a zero-cost entry follows the last segment");
-    if (wave == 0) build_segments<BM, TM, WGM>(a, lane, s_tab, &s_R1, &s_C1);
+    if (wave == 0) build_segments<MODE, BM, TM, WGM>(a, lane, s_tab, &s_R1, &s_C1);
     __syncthreads();
     if (wave == 0) xcd_bounds(a, s_tab, s_R1, s_C1, lane, s_bound);
     __syncthreads();
