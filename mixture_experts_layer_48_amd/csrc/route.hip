@@ -523,7 +523,9 @@ __global__ __launch_bounds__(256) void rank_sort_kernel(const float* __restrict_
 // its own, before the next pass reads them): the vector memory counter counts stores too, so a
 // store issued just before the next chunk's loads are needed would make them wait for it.
 //
-// Proposal counts are per wave, stamped with the round number, so no round has to clear them;
+// Proposal counts are per wave (ballot matching), stamped with the round number, so no round
+// has to clear them, and an LDS total per expert (the two totals alternate between rounds) lets
+// the proposers of an expert with no more proposals than room accept without reading them;
 // after round_limit rounds (at most 0xFFFF, the stamp's width) the counts are cleared and the
 // stamps start again at 1, at the top of a round, when no earlier round's count is read any more.
 // Whether another round follows needs no block reduction: each wave's "a proposal was turned
@@ -531,7 +533,7 @@ __global__ __launch_bounds__(256) void rank_sort_kernel(const float* __restrict_
 #define CAP_THREADS 1024
 #define CAP_WIN 4                   // 16-byte pieces (16 ranks each) of a token's list in LDS
 
-template <int THREADS>
+template <int THREADS, int BITS>
 __global__ __launch_bounds__(THREADS) void capacity_kernel(
     const uint8_t* __restrict__ ranked, uint8_t* __restrict__ rpos, int T, int N, int NP, int CT, int k,
     int C, uint32_t round_limit, int32_t* __restrict__ idx) {
@@ -544,12 +546,14 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
     __shared__ int fill[MOE_MAX_EXPERTS];
     __shared__ int16_t lim[MOE_MAX_EXPERTS];            // chunk-local cut-off, -1: full at chunk start
     __shared__ u32x4 rejw[CAP_WAVES_ / 4];              // per wave: a proposal was turned away
+    __shared__ int tot[2][MOE_MAX_EXPERTS];             // proposals per expert, rounds alternating
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = tid >> 6;
     const int NQ = NP >> 2;               // words per ranked row (multiple of 4)
     const int NPC = NQ >> 2;              // 16-rank pieces per ranked row
     for (int e = tid; e < MOE_MAX_EXPERTS; e += CAP_THREADS_) fill[e] = 0;
     for (int i = tid; i < CAP_WAVES_ * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&cnt[0][0])[i] = 0u;
+    for (int i = tid; i < 2 * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&tot[0][0])[i] = 0;
     uint32_t round = 0;                   // stamp of the current round's counts, 1 .. round_limit
 
     // next chunk's state, fetched during the current chunk: for this thread's token the first
@@ -616,6 +620,8 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                 // barrier that ended the previous round follows its last read of cnt
                 if (round >= round_limit) {
                     for (int i = tid; i < CAP_WAVES_ * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&cnt[0][0])[i] = 0u;
+                    // the restarted stamps may give two rounds in a row the same parity
+                    for (int i = tid; i < 2 * MOE_MAX_EXPERTS; i += CAP_THREADS_) (&tot[0][0])[i] = 0;
                     round = 0;
                     __syncthreads();                      // cleared before any new stamp is written
                 }
@@ -673,12 +679,20 @@ __global__ __launch_bounds__(THREADS) void capacity_kernel(
                 }
                 // per-wave proposal counts (ballot matching), written once per expert and wave
                 const uint32_t v = (uint32_t)(choice + 1);
-                const uint64_t eq = match_lanes<9>(v);
+                const uint64_t eq = match_lanes<BITS>(v);
                 const int rin = __popcll(eq & lanemask_lt());
-                if (choice >= 0 && rin == 0) cnt[wave][choice] = (round << 16) | (uint32_t)__popcll(eq);
+                if (choice >= 0 && rin == 0) {
+                    cnt[wave][choice] = (round << 16) | (uint32_t)__popcll(eq);
+                    atomicAdd(&tot[round & 1][choice], __popcll(eq));
+                }
                 __syncthreads();
+                // the other round's totals start again from zero: last read before this round's
+                // first barrier, next added to after its second
+                for (int e = tid; e < MOE_MAX_EXPERTS; e += CAP_THREADS_) tot[(round + 1) & 1][e] = 0;
                 bool rejected = false;
-                if (choice >= 0) {
+                // an expert with no more proposals than room keeps them all: its proposers skip
+                // the per-wave counts
+                if (choice >= 0 && tot[round & 1][choice] > C - fill[choice]) {
                     // proposals to the same expert from earlier waves: every wave's count read at
                     // once, then the earlier ones added
                     uint32_t cw[CAP_WAVES_];
@@ -851,7 +865,8 @@ hipError_t launch_capacity(const float* z, uint8_t* ranked, int T, int N, int k,
     if (e != hipSuccess) return e;
     // one token per thread and chunk (the ranked-list windows of 1024 tokens take 64 KiB of LDS)
     const int CT = CAP_THREADS;
-    auto kern = capacity_kernel<CAP_THREADS>;
+    // ballot matching on choice + 1 <= N: 8 bits below 256 experts
+    auto kern = N < 256 ? capacity_kernel<CAP_THREADS, 8> : capacity_kernel<CAP_THREADS, 9>;
     hipLaunchKernelGGL(kern, dim3(1), dim3(CAP_THREADS), 0, s, ranked, ranked + (size_t)T * NP, T, N, NP, CT,
                        k, C, capacity_round_limit(), idx);
     e = hipGetLastError();
