@@ -165,7 +165,8 @@ moe_status moe_permute(const moe_layer_desc *desc, const int32_t *idx, int32_t *
  *   (the slot's gate weight, [T * k] fp32).  With has_shared, rows T*k .. T*k + T - 1 hold
  *   the shared expert's output for tokens 0 .. T-1 (never scaled).
  *   y_perm: [(T * k + (has_shared ? T : 0)), d] fp32; rows not listed above are left
- *   untouched.  ws: workspace (hidden state H). */
+ *   untouched.  ws: workspace (hidden state H, then the grouped GEMMs' schedule: tile-claim counters
+ *   and a table of the tiles); moe_workspace_size(desc) bytes always suffice. */
 moe_status moe_expert_ffn(const moe_layer_desc *desc, const moe_weights *weights,
                           const void *x, const int32_t *perm, const int32_t *offsets,
                           const float *row_scale, void *y_perm, void *ws, size_t ws_bytes,

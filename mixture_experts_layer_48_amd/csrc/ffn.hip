@@ -39,7 +39,13 @@ struct FfnKArgs {
     int T, k, N, has_shared, K, Ncols, mt_max, n_tiles;
     int ksplit;             // K is split into ksplit equal parts (out-projection only)
     long long part_stride;  // elements between the fp32 partial outputs of the K parts
+    unsigned int* ctr;      // claiming GEMM: its schedule memory, 8 claim counters and from
+                            // word FFN_CTR_BYTES / 4 on the tile table (ffn_tile_table)
 };
+
+__device__ __forceinline__ int4* tile_table(const FfnKArgs& a) {
+    return (int4*)((char*)a.ctr + FFN_CTR_BYTES);
+}
 
 // Tile configuration: BM rows x BNH output columns per block, WGM x WGN waves; each wave owns a
 // (BM/WGM) x (BNH/WGN) block of outputs (for SwiGLU: of both the gate and the up products).
@@ -66,9 +72,14 @@ struct FfnTile {
 // of the numbering (block b runs on XCD b % 8).
 //
 // The kernel is persistent: the grid holds only as many blocks as the CUs keep resident, and
-// each block runs a sequence of tiles.  Within an XCD's range, round i of tiles goes to the
-// XCD's blocks in order, reversed on odd rounds, so that a pattern of period two (a full m-tile
-// next to an expert's short last one) does not fall on the same blocks every round.
+// each block runs a sequence of tiles from its XCD's range.  The in-projections (and 128-row
+// tiles) deal the range: round i of it to the XCD's blocks in order, reversed on odd rounds, so
+// that a pattern of period two (a full m-tile next to an expert's short last one) does not fall
+// on the same blocks every round.  The out-projection with 256- and 320-row tiles claims tiles
+// one at a time with an atomic counter per range (the XCD's blocks take the range in order, so
+// the tiles in flight together still form the rectangles above) and, once its own range is used
+// up, from the other XCDs' ranges: a block that runs faster (a shorter tile, a less contended CU)
+// takes more, instead of the launch waiting for the slowest share.
 #define FFN_MAX_SEG 320   // 5 segments per lane of one wave: routed experts and the shared one
 
 // Sub-tiles per wave of the variant a tile with nsub valid 32-row sub-tiles runs: the fewest of
@@ -224,6 +235,34 @@ __device__ __forceinline__ TileInfo decode_lane(const FfnKArgs& a, const int* s_
     return ti;
 }
 
+// The tile table of one tiled GEMM launch, in the numbering its blocks claim tiles by: entry t =
+// {segment | K part << 16, m-tile, n-tile, 0}.  One wave per block, each with
+// a segment table of its own; block 0 also clears the launch's eight claim counters.  The GEMM
+// then turns a claimed tile number into a tile with one load, issued a stage before it is used,
+// instead of a search and a chain of divisions inside a stage.
+template <int MODE, int BM, int BNH, int WGM, int WGN>
+__global__ __launch_bounds__(64) void ffn_tile_table(FfnKArgs a) {
+    constexpr int TM = FfnTile<MODE, BM, BNH, WGM, WGN>::TM;
+    __shared__ int s_tab[5 * FFN_MAX_SEG];
+    __shared__ int s_R1, s_C1;
+    const int lane = threadIdx.x;
+    if (blockIdx.x == 0 && lane < 8) a.ctr[lane] = 0u;
+    build_segments<MODE, BM, TM, WGM>(a, lane, s_tab, &s_R1, &s_C1);
+    __syncthreads();
+    const int R1 = s_R1, R = R1 * a.ksplit;
+    for (int t = blockIdx.x * 64 + lane; t < R; t += gridDim.x * 64) {
+        const TileInfo ti = decode_lane(a, s_tab, R1, t);
+        tile_table(a)[t] = make_int4(ti.seg | (ti.kpart << 16), ti.mt, ti.nt, 0);
+    }
+}
+
+// Which tiled GEMMs claim their tiles: the out-projection with 256- and 320-row tiles.  Measured
+// on one box (down projection, ms, dealt -> claimed): Mixtral 0.949 -> 0.924, DeepSeek-V3 2.615
+// -> 2.53, shared + top-7 of 256 2.43 -> 2.40, top-1 of 16 0.651 -> 0.638, skewed 0.83 -> 0.82;
+// but top-1 of 128 (32 rows per expert, 128-row tiles, a weight stream) 2.53 -> 2.59.  The
+// gate/up projection claiming its tiles was no faster, and its larger register footprint put
+// spill reloads into its main loops.
+constexpr bool claims_tiles(int mode, int bm) { return mode == MODE_OUT && bm >= 256; }
 template <int MODE, int BM, int BNH, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     using Cfg = FfnTile<MODE, BM, BNH, WGM, WGN>;
@@ -245,7 +284,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     __shared__ int s_tab[5 * FFN_MAX_SEG];
     __shared__ int s_R1, s_C1;
     __shared__ int s_bound[9];                                 // the XCDs' shares of the tiles
-    __shared__ int s_tiles[64 * 6];                            // this block's next 64 tiles
+    __shared__ int s_tiles[64 * 6];                            // dealt tiles, or the ring of claimed ones
     __shared__ int s_src[MODE == MODE_OUT ? 1 : BM];          // next tile's x row of each A row
     __shared__ float s_scale[MODE == MODE_OUT ? 2 * BM : 1];  // gate weight of each row, 2 tiles
 
@@ -257,13 +296,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     if (wave == 0) xcd_bounds(a, s_tab, s_R1, s_C1, lane, s_bound);
     __syncthreads();
     const int R1 = __builtin_amdgcn_readfirstlane(s_R1);
-    const int nbx = gridDim.x >> 3, xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
-    const int lo = __builtin_amdgcn_readfirstlane(s_bound[xcd]), hi = __builtin_amdgcn_readfirstlane(s_bound[xcd + 1]);
-    auto tile_id = [&](int i) { return lo + i * nbx + ((i & 1) ? nbx - 1 - jb : jb); };
+    const int xcd = blockIdx.x & 7;
     int it = 0;                                          // tiles done by this block
-    if (tile_id(0) >= hi) return;
-    // wave 0 decodes this block's tiles 64 at a time, one per lane, into s_tiles
-    auto decode_chunk = [&](int c) {
+    // A block's tiles are claimed (DYN) or dealt.  Dealt: round i of the XCD's range goes to its
+    // blocks in order, reversed on odd rounds, and wave 0 decodes the block's tiles 64 at a time,
+    // one per lane, into s_tiles.  Claimed, by wave 0: the XCD's own range first, then the others
+    // in turn, each by an add on the range's counter; a claimed tile's entry comes from the tile
+    // table into a ring of four slots.  `first` is the result of an add already issued on this
+    // XCD's counter (~0u: none).  A counter past its range's end stays so (claims only add), so a
+    // range found used up is not asked again.
+    constexpr bool DYN = claims_tiles(MODE, BM);
+    const int lo = __builtin_amdgcn_readfirstlane(s_bound[xcd]), hi = __builtin_amdgcn_readfirstlane(s_bound[xcd + 1]);
+    const int nbx = gridDim.x >> 3, jb = blockIdx.x >> 3;
+    auto tile_id = [&](int i) { return lo + i * nbx + ((i & 1) ? nbx - 1 - jb : jb); };
+    auto decode_chunk = [&](int c) {                     // wave 0, dealt tiles 64c .. 64c + 63
         const int t = tile_id(c * 64 + lane);
         if (t < hi) {
             const TileInfo ti = decode_lane(a, s_tab, R1, t);
@@ -271,20 +317,88 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
             p[0] = ti.seg; p[1] = ti.mt; p[2] = ti.nt; p[3] = ti.kpart; p[4] = ti.row_beg; p[5] = ti.row_end;
         }
     };
+    unsigned int spent = 0;                              // ranges found used up
+    auto claim = [&](unsigned int first) -> int {
+#pragma unroll 1
+        for (int v = 0; v < 8; ++v) {
+            const int x = (xcd + v) & 7;
+            if (spent & (1u << x)) continue;
+            unsigned int c = first;
+            if (v != 0 || first == ~0u) {
+                if (lane == 0) c = atomicAdd(a.ctr + x, 1u);
+                c = __builtin_amdgcn_readfirstlane(c);
+            }
+            const int t = s_bound[x] + (int)c;
+            if (t < s_bound[x + 1]) return t;
+            spent |= 1u << x;
+        }
+        return -1;
+    };
+    // Ring slot i & 3 (claimed tiles): the table entry of the block's tile i (word w from lane w
+    // of wave 0) and whether one was found (tile number t >= 0).
+    auto fetch = [&](int t) -> int {                     // wave 0: this lane's word of entry t
+        return (t >= 0 && lane < 4) ? ((const int*)tile_table(a))[4 * t + lane] : 0;
+    };
+    auto put = [&](int i, int t, int e) {                // wave 0
+        int* p = s_tiles + (i & 3) * 5;
+        if (lane < 4) p[lane] = e;
+        if (lane == 4) p[4] = t >= 0 ? 1 : 0;
+    };
+    auto found = [&](int i) { return __builtin_amdgcn_readfirstlane(s_tiles[(i & 3) * 5 + 4]) != 0; };
     auto read_tile = [&](int i) {
-        const int* p = s_tiles + (i & 63) * 6;
         TileInfo ti;
-        ti.seg = __builtin_amdgcn_readfirstlane(p[0]);
-        ti.mt = __builtin_amdgcn_readfirstlane(p[1]);
-        ti.nt = __builtin_amdgcn_readfirstlane(p[2]);
-        ti.kpart = __builtin_amdgcn_readfirstlane(p[3]);
-        ti.row_beg = __builtin_amdgcn_readfirstlane(p[4]);
-        ti.row_end = __builtin_amdgcn_readfirstlane(p[5]);
+        if constexpr (DYN) {
+            const int* p = s_tiles + (i & 3) * 5;
+            const int w0 = __builtin_amdgcn_readfirstlane(p[0]);
+            ti.seg = w0 & 0xffff;
+            ti.kpart = w0 >> 16;
+            ti.mt = __builtin_amdgcn_readfirstlane(p[1]);
+            ti.nt = __builtin_amdgcn_readfirstlane(p[2]);
+            ti.row_beg = __builtin_amdgcn_readfirstlane(s_tab[2 * FFN_MAX_SEG + ti.seg]);
+            ti.row_end = __builtin_amdgcn_readfirstlane(s_tab[3 * FFN_MAX_SEG + ti.seg]);
+        } else {
+            const int* p = s_tiles + (i & 63) * 6;
+            ti.seg = __builtin_amdgcn_readfirstlane(p[0]);
+            ti.mt = __builtin_amdgcn_readfirstlane(p[1]);
+            ti.nt = __builtin_amdgcn_readfirstlane(p[2]);
+            ti.kpart = __builtin_amdgcn_readfirstlane(p[3]);
+            ti.row_beg = __builtin_amdgcn_readfirstlane(p[4]);
+            ti.row_end = __builtin_amdgcn_readfirstlane(p[5]);
+        }
         return ti;
     };
-    if (wave == 0) decode_chunk(0);
-    __syncthreads();
+    if constexpr (DYN) {
+        if (wave == 0) {
+            const int t0 = claim(~0u);
+            put(0, t0, fetch(t0));
+            const int t1 = claim(~0u);
+            put(1, t1, fetch(t1));
+        }
+        __syncthreads();
+        if (!found(0)) return;                           // every range used up already
+    } else {
+        if (tile_id(0) >= hi) return;
+        if (wave == 0) decode_chunk(0);
+        __syncthreads();
+    }
     TileInfo cur = read_tile(0);
+    // Tile it + 2 of the block: claimed with an add issued at the start of tile it, its table
+    // entry loaded after the tile's first stage and put in its slot after the second (whose
+    // wait for its own loads covers it).  The stages that follow end in barriers, so the slot
+    // is visible when tile it + 1 starts; it was last read when tile it - 2 started.
+    unsigned int pend = ~0u;
+    bool claim_next = false;
+    auto fetch_next = [&](int& t, int& e) {
+        t = -1;
+        e = 0;
+        if (DYN && claim_next && wave == 0) {
+            t = claim(pend);
+            e = fetch(t);
+        }
+    };
+    auto put_next = [&](int t, int e) {
+        if (DYN && claim_next && wave == 0) put(it + 2, t, e);
+    };
 
     const int KT = a.K / FB_BK / a.ksplit;               // stages of one tile
     // A tile's last two stages load the next tile's first stage (and half of its second) into
@@ -587,7 +701,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
         if (chain) {
             stage(acc, st0, st1, 1, 2, fa, fb, nv, first_step);
             after_first_stage();
+            int tn, en;
+            fetch_next(tn, en);
             stage(acc, st1, st0, 2, 3, fa, fb, nv, later_step);
+            put_next(tn, en);
             for (int kt = 2; kt + 4 <= KT; kt += 2) {
                 stage(acc, st0, st1, kt + 1, kt + 2, fa, fb, nv, later_step);
                 stage(acc, st1, st0, kt + 2, kt + 3, fa, fb, nv, later_step);
@@ -606,6 +723,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
                     for (int j = 0; j < TN; ++j)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
+            // (no chain: the next tile starts after a barrier, which makes the slot visible)
+            int tn, en;
+            fetch_next(tn, en);
+            put_next(tn, en);
             int kt = 0;
             for (; kt + 2 <= KT; kt += 2) {
                 stage(acc, st0, st1, kt + 1, kt + 2, fa, fb, nv, later_step);
@@ -635,11 +756,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     issue_part(st0, 0, 0, NLD, std::integral_constant<int, TM>{});
     issue_part(st1, 1, 0, NLD0, std::integral_constant<int, TM>{});
     for (;;) {
-        const bool has_next = tile_id(it + 1) < hi;
-        if (has_next && ((it + 1) & 63) == 0) {
-            // every wave has taken its tiles of the previous 64 from s_tiles (one tile back)
-            if (wave == 0) decode_chunk((it + 1) >> 6);
-            __syncthreads();
+        bool has_next;
+        if constexpr (DYN) {
+            has_next = found(it + 1);
+            // without a next tile every range is used up: no claim (it could only fail)
+            claim_next = has_next;
+            pend = ~0u;
+            if (has_next && wave == 0 && !(spent & (1u << xcd))) {
+                if (lane == 0) pend = atomicAdd(a.ctr + xcd, 1u);
+                pend = __builtin_amdgcn_readfirstlane(pend);
+            }
+        } else {
+            has_next = tile_id(it + 1) < hi;
+            if (has_next && ((it + 1) & 63) == 0) {
+                // every wave has taken its tiles of the previous 64 from s_tiles (one tile back)
+                if (wave == 0) decode_chunk((it + 1) >> 6);
+                __syncthreads();
+            }
         }
         nx = has_next ? read_tile(it + 1) : cur;
         kbase_n = nx.kpart * KT * FB_BK;
@@ -970,8 +1103,24 @@ static int resident_blocks(K kern, int threads) {
     return v;
 }
 
+// Tiles of a tiled GEMM launch at most: m-tiles (an expert's rows in tiles of BM, the shared
+// expert's T rows too) x n-tiles x K parts.
+static long long tile_bound(int T, int k, int N, int has_shared, int Ncols, int ksplit, int BM, int BNH) {
+    const long long mt = ((long long)T * k + BM - 1) / BM + N + (has_shared ? (T + BM - 1) / BM : 0);
+    return mt * ((Ncols + BNH - 1) / BNH) * (ksplit < 1 ? 1 : ksplit);
+}
+
+// Schedule memory of the two tiled GEMMs: claim counters (in-projection 0..7, out-projection
+// 16..23), then one tile table, which the out-projection's launch rewrites after the
+// in-projection's GEMM has run.  Sized for the smallest tiles (128 x 128) and both projections.
+size_t ffn_sched_bytes(int T, int k, int N, int d, int d_ff, int has_shared, int ksplit) {
+    const long long in = tile_bound(T, k, N, has_shared, d_ff, 1, 128, 128);
+    const long long out = tile_bound(T, k, N, has_shared, d, ksplit, 128, 128);
+    return FFN_CTR_BYTES + 16 * (size_t)(in > out ? in : out);
+}
+
 template <int MODE, int BM, int BNH, int WGM, int WGN>
-static hipError_t launch_bf16(const FfnKArgs& ka, hipStream_t s) {
+static hipError_t launch_bf16(const FfnKArgs& ka, size_t sched_bytes, hipStream_t s) {
     using Cfg = FfnTile<MODE, BM, BNH, WGM, WGN>;
     auto kern = ffn_bf16_kernel<MODE, BM, BNH, WGM, WGN>;
     FfnKArgs a = ka;
@@ -980,7 +1129,16 @@ static hipError_t launch_bf16(const FfnKArgs& ka, hipStream_t s) {
     a.n_tiles = (a.Ncols + BNH - 1) / BNH;
     const int resident = resident_blocks(kern, Cfg::NT);
     if (resident <= 0) return hipErrorInvalidDevice;
-    long long G = 8 * (((long long)a.mt_max * a.n_tiles * a.ksplit + 7) / 8);   // one tile per block at most
+    const long long tiles = (long long)a.mt_max * a.n_tiles * a.ksplit;
+    if (claims_tiles(MODE, BM)) {
+        if (!a.ctr || FFN_CTR_BYTES + 16 * (size_t)tiles > sched_bytes) return hipErrorInvalidValue;
+        const long long GT = (tiles + 63) / 64;         // table: one entry per lane, <= 256 blocks
+        hipLaunchKernelGGL((ffn_tile_table<MODE, BM, BNH, WGM, WGN>), dim3((unsigned)(GT < 256 ? GT : 256)), dim3(64),
+                           0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    long long G = 8 * ((tiles + 7) / 8);                // one tile per block at most
     if (G > resident) G = resident;
     hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), 0, s, a);
     return hipGetLastError();
@@ -1040,19 +1198,20 @@ hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
         a.C = f.h;
         a.T = f.T; a.k = f.k; a.N = f.N; a.has_shared = f.has_shared;
         a.K = f.d; a.Ncols = f.d_ff;
+        a.ctr = f.ctr;
         if (f.ffn == 1) {
             a.B0 = (const bf16*)f.w_gate; a.B1 = (const bf16*)f.w_up;
             a.S0 = (const bf16*)f.sh_gate; a.S1 = (const bf16*)f.sh_up;
             if (skinny(f)) return launch_skinny<MODE_IN_SWIGLU, SK_U_IN, SK_CG_IN>(a, s);
-            if (tiles_320(f)) return launch_bf16<MODE_IN_SWIGLU, 320, 128, 2, 4>(a, s);
-            if (big_tiles(f)) return launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, s);
-            return launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, s);
+            if (tiles_320(f)) return launch_bf16<MODE_IN_SWIGLU, 320, 128, 2, 4>(a, f.sched_bytes, s);
+            if (big_tiles(f)) return launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, f.sched_bytes, s);
+            return launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, f.sched_bytes, s);
         }
         a.B0 = (const bf16*)f.w_up;
         a.S0 = (const bf16*)f.sh_up;
         if (skinny(f)) return launch_skinny<MODE_IN_RELU, SK_U_IN, SK_CG_IN>(a, s);
-        if (big_tiles(f)) return launch_bf16<MODE_IN_RELU, 256, 256, 2, 2>(a, s);
-        return launch_bf16<MODE_IN_RELU, 128, 128, 2, 2>(a, s);
+        if (big_tiles(f)) return launch_bf16<MODE_IN_RELU, 256, 256, 2, 2>(a, f.sched_bytes, s);
+        return launch_bf16<MODE_IN_RELU, 128, 128, 2, 2>(a, f.sched_bytes, s);
     }
     const long long n = rows_total * f.d_ff;
     const dim3 grid((unsigned)((n + 255) / 256));
@@ -1082,13 +1241,14 @@ hipError_t launch_ffn_out(const FfnLaunch& f, hipStream_t s) {
         a.K = f.d_ff; a.Ncols = f.d;
         a.ksplit = f.ksplit;
         a.part_stride = (long long)((long long)f.T * f.k + (f.has_shared ? f.T : 0)) * f.d;
+        a.ctr = f.ctr;
         if (skinny(f)) return launch_skinny<MODE_OUT, SK_U_OUT, SK_CG_OUT>(a, s);
         // eight waves (2 x 4, two per SIMD) for the out-projection: measured on the same box,
         // Mixtral down projection 0.94 vs 1.01 ms with four, skewed 0.89 vs 0.93, DeepSeek-V3
         // 2.72 vs 2.71; four stay faster for the SwiGLU in-projection (1.70 vs 1.59 ms)
-        if (tiles_320_out(f)) return launch_bf16<MODE_OUT, 320, 256, 2, 4>(a, s);
-        if (big_tiles(f)) return launch_bf16<MODE_OUT, 256, 256, 2, 4>(a, s);
-        return launch_bf16<MODE_OUT, 128, 128, 2, 2>(a, s);
+        if (tiles_320_out(f)) return launch_bf16<MODE_OUT, 320, 256, 2, 4>(a, f.sched_bytes, s);
+        if (big_tiles(f)) return launch_bf16<MODE_OUT, 256, 256, 2, 4>(a, f.sched_bytes, s);
+        return launch_bf16<MODE_OUT, 128, 128, 2, 2>(a, f.sched_bytes, s);
     }
     const long long rows_total = (long long)f.T * f.k + (f.has_shared ? f.T : 0);
     const long long n = rows_total * f.d;

@@ -93,9 +93,14 @@ int ksplit_of(const moe_layer_desc& d) {
     return ffn_out_ksplit(d.T, d.k, d.N, d.d, d.d_ff, d.has_shared, d.dtype);
 }
 
+// the grouped GEMMs' schedule memory: claim counters, then a tile table
+size_t sched_bytes(const moe_layer_desc& d, int ksplit) {
+    return align256(ffn_sched_bytes(d.T, d.k, d.N, d.d, d.d_ff, d.has_shared, ksplit));
+}
+
 // Workspace of the whole forward, carved in this order (each piece 256-byte aligned).
 struct Layout {
-    size_t z, ranked, idx, w, counts, offsets, perm, inv, h, yp, total;
+    size_t z, ranked, idx, w, counts, offsets, perm, inv, h, yp, ctr, total;
 };
 Layout layout_of(const moe_layer_desc& d) {
     Layout L{};
@@ -114,6 +119,8 @@ Layout layout_of(const moe_layer_desc& d) {
                            align256(router_workspace_bytes(d.T, d.d, d.N, d.dtype)));
     // fp32 expert rows, one copy per K part of the out-projection
     L.yp = o; o += align256((size_t)rows_total(d) * d.d * 4 * ksplit_of(d));
+    // the grouped GEMMs' schedule: tile-claim counters and a tile table
+    L.ctr = o; o += sched_bytes(d, ksplit_of(d));
     // moe_routing_stats() reuses the workspace from offset 0 for its partial sums
     L.total = std::max(o, align256(stats_workspace_bytes(d.T, d.N)));
     return L;
@@ -123,8 +130,12 @@ size_t route_ws_bytes(const moe_layer_desc& d, bool have_logits) {
            (has_capacity(d) ? align256(capacity_workspace_bytes(d.T, d.N)) : 0) +
            align256(router_workspace_bytes(d.T, d.d, d.N, d.dtype));
 }
+// hidden state H, then the grouped GEMMs' schedule (one K part for the out-projection)
 size_t ffn_ws_bytes(const moe_layer_desc& d) {
-    return align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d));
+    return align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d)) + sched_bytes(d, 1);
+}
+unsigned int* ffn_ctr_of(const moe_layer_desc& d, void* ws) {
+    return (unsigned int*)((char*)ws + align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d)));
 }
 
 char* at(void* ws, size_t off) { return (char*)ws + off; }
@@ -246,6 +257,8 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights
         return fail(MOE_ERR_WORKSPACE, "workspace too small for moe_expert_ffn: need " + std::to_string(need));
     hipStream_t s = (hipStream_t)stream;
     FfnLaunch f = ffn_args(d, *weights, x, perm, offsets, row_scale, ws, y_perm);
+    f.ctr = ffn_ctr_of(d, ws);
+    f.sched_bytes = sched_bytes(d, 1);
     hipError_t e = launch_ffn_in(f, s);
     if (e != hipSuccess) return hip_fail(e, "ffn in-projection launch");
     e = launch_ffn_out(f, s);
@@ -301,6 +314,8 @@ moe_status forward_impl(const moe_layer_desc& d, const moe_weights& weights, con
     if (e != hipSuccess) return hip_fail(e, "permute launch");
     if ((st = record(ev(3), s)) != MOE_OK) return st;
     FfnLaunch f = ffn_args(d, weights, x, perm, offsets, w, h, yp);
+    f.ctr = (unsigned int*)at(ws, L.ctr);
+    f.sched_bytes = sched_bytes(d, ksplit_of(d));
     if (q4) f.q4 = *q4;
     f.ksplit = q4 ? 1 : ksplit_of(d);
     e = q4 ? launch_ffn_in_q4(f, s) : launch_ffn_in(f, s);

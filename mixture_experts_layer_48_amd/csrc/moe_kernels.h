@@ -48,9 +48,13 @@ struct FfnLaunch {
     void* h;                  // [T*k + T, d_ff] hidden state
     void* y_perm;             // [ksplit][T*k + T, d] fp32 (ksplit partial sums)
     int ksplit;               // K parts of the out-projection (1 = y_perm holds the result)
+    unsigned int* ctr;        // the tiled GEMMs' schedule memory (claim counters, then a tile
+    size_t sched_bytes;       // table), sched_bytes >= ffn_sched_bytes(); set up by the launches
     FfnQ4Weights q4;          // int4 weights (the q4 launchers only)
 };
 int ffn_out_ksplit(int T, int k, int N, int d, int d_ff, int has_shared, int dtype);
+#define FFN_CTR_BYTES 256
+size_t ffn_sched_bytes(int T, int k, int N, int d, int d_ff, int has_shared, int ksplit);
 hipError_t launch_ffn_in(const FfnLaunch& a, hipStream_t s);   // H = act(x W_in)
 hipError_t launch_ffn_out(const FfnLaunch& a, hipStream_t s);  // y_perm = scale * H W_out
 hipError_t launch_combine(const void* y_perm, const int32_t* inv, const float* w, void* y, int T,
