@@ -21,6 +21,7 @@
 
 #define PM_THREADS 1024
 #define PM_WAVES (PM_THREADS / 64)
+#define PM_BATCH 16   // groups of 64 slots whose expert ids one wave loads together
 
 // Destination-major keys for the expert-parallel send layout: experts are ordered by (owner
 // rank, expert id); pos[e] is expert e's place in that order, exp_at inverts it, and rank r's
@@ -61,9 +62,23 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
         if constexpr (EP) return s_pos[e];
         return e;
     };
-    for (int s = beg + lane; s < end; s += 64) {
-        const int e = key_of(idx[s]);
-        if (e >= 0) atomicAdd(&hist[wave][e], 1);  // integer counts: order-independent
+    // A lane's slots are beg + lane + 64 g.  Their ids are loaded PM_BATCH groups at a time, all
+    // loads of a batch in flight together (one at a time, each load's latency was paid in turn).
+    auto load_batch = [&](int g0, int (&ev)[PM_BATCH]) {
+#pragma unroll
+        for (int u = 0; u < PM_BATCH; ++u) {
+            const int s = beg + g0 + u * 64 + lane;
+            ev[u] = s < end ? idx[s] : -1;
+        }
+    };
+    for (int g0 = 0; g0 < per_wave; g0 += 64 * PM_BATCH) {
+        int ev[PM_BATCH];
+        load_batch(g0, ev);
+#pragma unroll
+        for (int u = 0; u < PM_BATCH; ++u) {
+            const int e = key_of(ev[u]);
+            if (e >= 0) atomicAdd(&hist[wave][e], 1);  // integer counts: order-independent
+        }
     }
     __syncthreads();
     if (tid < 64) {  // one wave: totals, exclusive scan over places
@@ -119,10 +134,16 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
         }
     }
     __syncthreads();
-    for (int g = 0; g < per_wave; g += 64) {
+    for (int g0 = 0; g0 < per_wave; g0 += 64 * PM_BATCH) {
+      int ev[PM_BATCH];
+      load_batch(g0, ev);
+#pragma unroll
+      for (int u = 0; u < PM_BATCH; ++u) {
+        const int g = g0 + u * 64;
+        if (g >= per_wave) break;                        // uniform: past the wave's range
         const int s = beg + g + lane;
         const bool valid = s < end;
-        const int e = valid ? key_of(idx[s]) : -1;
+        const int e = valid ? key_of(ev[u]) : -1;
         const uint64_t eq = match_lanes<9>((uint32_t)(e + 1));
         const uint64_t lt = lanemask_lt();
         if (e >= 0) {
@@ -141,6 +162,7 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
             hist[wave][e] += __popcll(eq);
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
+      }
     }
 }
 
