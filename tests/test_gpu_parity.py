@@ -89,6 +89,14 @@ SMALL = {
     # every token is checked
     "multi_tile_blocks": W.LayerConfig("multi_tile_blocks", T=4096, d=512, N=32, k=2, d_ff=2048, dtype="bf16",
                                        ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=27),
+    # 512 rows per expert: 256-row out-projection tiles, 512 of them, so every block claims
+    # several in a row (its XCD range's counter, then the other XCDs' ranges), decoded from the
+    # tile table; K of 4 stages (the next tile's first stages loaded by the current tile's last
+    # ones) and of 3 (no chaining: the next tile loaded after a barrier)
+    "claimed_out_chain": W.LayerConfig("claimed_out_chain", T=4096, d=4096, N=16, k=2, d_ff=256, dtype="bf16",
+                                       ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=29),
+    "claimed_out_nochain": W.LayerConfig("claimed_out_nochain", T=4096, d=4096, N=16, k=2, d_ff=192, dtype="bf16",
+                                         ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, seed=30),
     # capacity with 256 experts: scans that run past the ranked-list window kept in LDS (picks
     # deeper than 64 ranks), with slots dropped once every expert is full, and without drops
     "capacity_deep_drops": W.LayerConfig("capacity_deep_drops", T=300, d=64, N=256, k=2, d_ff=64, dtype="bf16",
