@@ -1110,9 +1110,9 @@ static long long tile_bound(int T, int k, int N, int has_shared, int Ncols, int 
     return mt * ((Ncols + BNH - 1) / BNH) * (ksplit < 1 ? 1 : ksplit);
 }
 
-// Schedule memory of the two tiled GEMMs: claim counters (in-projection 0..7, out-projection
-// 16..23), then one tile table, which the out-projection's launch rewrites after the
-// in-projection's GEMM has run.  Sized for the smallest tiles (128 x 128) and both projections.
+// Schedule memory of the tiled GEMMs: eight claim counters, then one tile table; a claiming
+// GEMM's launch writes both (ffn_tile_table) just before the GEMM, so successive launches on one
+// stream can share them.  Sized for the smallest tiles (128 x 128) and either projection.
 size_t ffn_sched_bytes(int T, int k, int N, int d, int d_ff, int has_shared, int ksplit) {
     const long long in = tile_bound(T, k, N, has_shared, d_ff, 1, 128, 128);
     const long long out = tile_bound(T, k, N, has_shared, d, ksplit, 128, 128);
