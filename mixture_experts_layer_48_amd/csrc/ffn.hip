@@ -39,6 +39,8 @@ struct FfnKArgs {
     int T, k, N, has_shared, K, Ncols, mt_max, n_tiles;
     int ksplit;             // K is split into ksplit equal parts (out-projection only)
     long long part_stride;  // elements between the fp32 partial outputs of the K parts
+    int small_rows;         // > 0: routed experts with 1 .. small_rows rows go to the weight-stream
+                            // kernel, and the tiled kernels leave them out
     unsigned int* ctr;      // claiming GEMM: its schedule memory, 8 claim counters and from
                             // word FFN_CTR_BYTES / 4 on the tile table (ffn_tile_table)
 };
@@ -116,6 +118,7 @@ __device__ __forceinline__ void build_segments(const FfnKArgs& a, int lane, int*
         if (s < a.N) {
             beg[q] = a.offsets[s];
             rows[q] = a.offsets[s + 1] - beg[q];
+            if (rows[q] <= a.small_rows) rows[q] = 0;      // (small_rows 0: none left out)
         } else if (s == a.N && a.has_shared) {
             beg[q] = a.T * a.k;
             rows[q] = a.T;
@@ -841,7 +844,7 @@ struct SkinnyTile {
 #ifndef SK_NT_MIN_CG
 #define SK_NT_MIN_CG 4
 #endif
-template <int MODE, int U, int CG>
+template <int MODE, int U, int CG, int RT>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
     using Tile = SkinnyTile<CG>;
     constexpr int NB = (MODE == MODE_IN_SWIGLU) ? 2 : 1;
@@ -870,6 +873,8 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
         if (NB == 2) B1 = a.S1;
     }
     if (row_end <= row_beg) return;                             // expert not touched
+    // with small_rows set, only the routed experts the tiled kernels leave out
+    if (a.small_rows > 0 && (seg >= a.N || row_end - row_beg > a.small_rows)) return;
     const int KS = a.K / 32 / nkp;                              // K steps of this wave
     const size_t step = (size_t)32 * a.Ncols;                   // elements between K steps
     B0 += (size_t)kp * KS * step;
@@ -896,19 +901,27 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
         else return *p;
     };
     const int kq = (lane >> 4) * 8;                             // this lane's K offset in a step
-    for (int m0 = row_beg; m0 < row_end; m0 += 16) {
-        const int r = m0 + (lane & 15);                         // this lane's A row
-        const bool rok = r < row_end;
-        int src;
-        if (MODE == MODE_OUT) src = rok ? r : m0;
-        else src = (seg < a.N) ? a.perm[rok ? r : m0] / a.k : (rok ? r : m0) - a.T * a.k;
-        const bf16* pa = a.A + (size_t)src * a.K + kq + kp * KS * 32;
-        f32x4 acc0[CG], acc1[CG];
+    // RT tiles of 16 rows per pass over the weights: row tile t's lane row m0 + 16 t + (lane & 15)
+    for (int m0 = row_beg; m0 < row_end; m0 += 16 * RT) {
+        bool rok[RT];
+        const bf16* pa[RT];
 #pragma unroll
-        for (int c = 0; c < CG; ++c) {
-            acc0[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            acc1[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < RT; ++t) {
+            const int r = m0 + 16 * t + (lane & 15);            // this lane's A row
+            rok[t] = r < row_end;
+            int src;
+            if (MODE == MODE_OUT) src = rok[t] ? r : m0;
+            else src = (seg < a.N) ? a.perm[rok[t] ? r : m0] / a.k : (rok[t] ? r : m0) - a.T * a.k;
+            pa[t] = a.A + (size_t)src * a.K + kq + kp * KS * 32;
         }
+        f32x4 acc0[RT][CG], acc1[RT][CG];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+                acc0[t][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                acc1[t][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
         const bf16x8 zero8 = {};
         // a K step's weight pieces into tile t, and back as B fragments
         struct Frag { bf16x8 b0[CG], b1[CG]; };
@@ -928,17 +941,20 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
                                                 4 * Tile::ROWB);
             }
         };
-        auto mfmas = [&](const Frag& f, const bf16x8& av) {
+        auto mfmas = [&](const Frag& f, const bf16x8 (&av)[RT]) {
 #pragma unroll
-            for (int c = 0; c < CG; ++c) {
-                acc0[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, f.b0[c], acc0[c], 0, 0, 0);
-                if (NB == 2) acc1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, f.b1[c], acc1[c], 0, 0, 0);
-            }
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int c = 0; c < CG; ++c) {
+                    acc0[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t], f.b0[c], acc0[t][c], 0, 0, 0);
+                    if (NB == 2)
+                        acc1[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t], f.b1[c], acc1[t][c], 0, 0, 0);
+                }
         };
         int ks = 0;
         for (; ks + U <= KS; ks += U) {
             u32x4 w0[U][CG], w1[U][CG];
-            bf16x8 av[U];
+            bf16x8 av[U][RT];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -946,7 +962,8 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
                     w0[u][q] = wload((const u32x4*)(pw0[q] + (ks + u) * step));
                     if (NB == 2) w1[u][q] = wload((const u32x4*)(pw1[q] + (ks + u) * step));
                 }
-                av[u] = rok ? *(const bf16x8*)(pa + (ks + u) * 32) : zero8;
+#pragma unroll
+                for (int t = 0; t < RT; ++t) av[u][t] = rok[t] ? *(const bf16x8*)(pa[t] + (ks + u) * 32) : zero8;
             }
             // every step's tile write and read go out before the MFMAs (steps alternate tiles)
             Frag f[U];
@@ -965,39 +982,43 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
                 w0[q] = wload((const u32x4*)(pw0[q] + ks * step));
                 if (NB == 2) w1[q] = wload((const u32x4*)(pw1[q] + ks * step));
             }
-            const bf16x8 av = rok ? *(const bf16x8*)(pa + ks * 32) : zero8;
+            bf16x8 av[RT];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) av[t] = rok[t] ? *(const bf16x8*)(pa[t] + ks * 32) : zero8;
             Frag f;
             to_tile(ks & 1, w0, w1);
             from_tile(ks & 1, f);
             mfmas(f, av);
         }
-        // 16x16 C layout: lane holds column (lane & 15), rows 4 * (lane >> 4) + i
+        // 16x16 C layout: lane holds column (lane & 15), rows 4 * (lane >> 4) + i of each row tile
 #pragma unroll
-        for (int c = 0; c < CG; ++c) {
-            const int col = (cg * CG + c) * 16 + (lane & 15);
-            if (col >= a.Ncols) continue;
+        for (int t = 0; t < RT; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = m0 + 4 * (lane >> 4) + i;
-                if (row >= row_end) continue;
-                if (MODE == MODE_OUT) {
-                    const float scale = (a.row_scale && seg < a.N) ? a.row_scale[a.perm[row]] : 1.0f;
-                    ((float*)a.C)[kp * a.part_stride + (size_t)row * a.Ncols + col] = acc0[c][i] * scale;
-                } else if (MODE == MODE_IN_SWIGLU) {
-                    ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)(silu_f32(acc0[c][i]) * acc1[c][i]);
-                } else {
-                    ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)fmaxf(acc0[c][i], 0.f);
+            for (int c = 0; c < CG; ++c) {
+                const int col = (cg * CG + c) * 16 + (lane & 15);
+                if (col >= a.Ncols) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = m0 + 16 * t + 4 * (lane >> 4) + i;
+                    if (row >= row_end) continue;
+                    if (MODE == MODE_OUT) {
+                        const float scale = (a.row_scale && seg < a.N) ? a.row_scale[a.perm[row]] : 1.0f;
+                        ((float*)a.C)[kp * a.part_stride + (size_t)row * a.Ncols + col] = acc0[t][c][i] * scale;
+                    } else if (MODE == MODE_IN_SWIGLU) {
+                        ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)(silu_f32(acc0[t][c][i]) * acc1[t][c][i]);
+                    } else {
+                        ((bf16*)a.C)[(size_t)row * a.Ncols + col] = (bf16)fmaxf(acc0[t][c][i], 0.f);
+                    }
                 }
             }
-        }
     }
 }
 
-template <int MODE, int U, int CG>
+template <int MODE, int U, int CG, int RT = 1>
 static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
     const int nkp = (MODE == MODE_OUT && a.ksplit > 1) ? a.ksplit : 1;
     const long long waves = (long long)(a.N + (a.has_shared ? 1 : 0)) * ((a.Ncols + 16 * CG - 1) / (16 * CG)) * nkp;
-    auto kern = ffn_skinny_kernel<MODE, U, CG>;
+    auto kern = ffn_skinny_kernel<MODE, U, CG, RT>;
     hipLaunchKernelGGL(kern, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
@@ -1023,6 +1044,21 @@ static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
 #define SK_CG_OUT 4
 #endif
 static bool skinny(const FfnLaunch& f) { return (long long)f.T * f.k <= 16LL * f.N; }
+// Next to the tiled SwiGLU gate/up GEMM, routed experts with at most FFN_SMALL_ROWS rows run as
+// weight streams, FFN_SMALL_RT tiles of 16 rows per pass over their weights (0: all in the tiled
+// GEMM): a tile of such an expert streams a whole weight slice through the tiled kernel's LDS
+// loads for a few rows, which the weight-stream kernel's register loads do faster.  Measured on
+// one box (gate/up, ms, tiled -> split): skewed with capacity 1.53 -> 1.46, top-1 of 128 SwiGLU
+// 5.55 -> 4.93, the other shapes unchanged.  The down projection and the ReLU in-projection were
+// slower split (skewed down 0.80 -> 0.86, top-1 of 128 ReLU 2.71 -> 2.89 and 2.54 -> 2.78): a
+// weight-stream wave re-reads its rows' activations for its own 64 columns, which against one
+// weight matrix (not the two of SwiGLU) costs as much as the weights themselves.
+#ifndef FFN_SMALL_ROWS
+#define FFN_SMALL_ROWS 64
+#endif
+#ifndef FFN_SMALL_RT
+#define FFN_SMALL_RT 4
+#endif
 
 // ------------------------------------------------------------------ fp32 path
 // One thread per output element, fp32 FMA in input order.  Used for fp32 layers.
@@ -1203,9 +1239,13 @@ hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
             a.B0 = (const bf16*)f.w_gate; a.B1 = (const bf16*)f.w_up;
             a.S0 = (const bf16*)f.sh_gate; a.S1 = (const bf16*)f.sh_up;
             if (skinny(f)) return launch_skinny<MODE_IN_SWIGLU, SK_U_IN, SK_CG_IN>(a, s);
-            if (tiles_320(f)) return launch_bf16<MODE_IN_SWIGLU, 320, 128, 2, 4>(a, f.sched_bytes, s);
-            if (big_tiles(f)) return launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, f.sched_bytes, s);
-            return launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, f.sched_bytes, s);
+            // (at 512 rows per expert on average, as on Mixtral, the launch would only cost time)
+            a.small_rows = (long long)f.T * f.k < 512LL * f.N ? FFN_SMALL_ROWS : 0;
+            const hipError_t e = tiles_320(f) ? launch_bf16<MODE_IN_SWIGLU, 320, 128, 2, 4>(a, f.sched_bytes, s)
+                               : big_tiles(f) ? launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, f.sched_bytes, s)
+                                              : launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, f.sched_bytes, s);
+            if (e != hipSuccess || a.small_rows == 0) return e;
+            return launch_skinny<MODE_IN_SWIGLU, SK_U_IN, SK_CG_IN, FFN_SMALL_RT>(a, s);
         }
         a.B0 = (const bf16*)f.w_up;
         a.S0 = (const bf16*)f.sh_up;

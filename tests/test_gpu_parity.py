@@ -172,6 +172,32 @@ def test_all_tokens_to_one_expert():
     _free()
 
 
+@pytest.mark.parametrize("T", [700, 1024])
+def test_small_experts_beside_the_tiled_gemm(T):
+    # The gate/up projection runs routed experts with at most 64 rows as weight streams beside the
+    # tiled GEMM (when experts average under 512 rows); here the loads sit at and around that
+    # bound: 64, 65, 63, 1 and 0 rows, the rest on three large experts (128-row tiles at T=700,
+    # 320-row tiles at T=1024).  A selection router (logit = x[t, e]) fixes each token's two
+    # experts; every token is checked.
+    cfg = W.LayerConfig(f"small_experts_{T}", T=T, d=128, N=8, k=2, d_ff=192, dtype="bf16", ffn=W.FFN_SWIGLU,
+                        gating=W.GATE_TOPK_SOFTMAX, seed=31)
+    inp = W.make_selection_router_inputs(cfg, "cuda")
+    small = [64, 65, 63, 1]                              # experts 0-3; expert 4 gets none
+    first = np.concatenate([np.full(n, e) for e, n in enumerate(small)] +
+                           [5 + np.arange(T - sum(small)) % 3]).astype(np.int64)
+    second = np.where(first >= 5, 5 + (first - 5 + 1) % 3, 5 + np.arange(T) % 3)
+    x = inp["x"]
+    x[:, :cfg.N] = -1.0
+    x[torch.arange(T, device="cuda"), torch.as_tensor(first, device="cuda")] = 1.5
+    x[torch.arange(T, device="cuda"), torch.as_tensor(second, device="cuda")] = 1.0
+    inp["logit_bias"] = None
+    layer, y, r = _full_parity(cfg, inp)
+    counts = r["counts"].cpu().numpy()
+    assert counts[:5].tolist() == [64, 65, 63, 1, 0], counts
+    assert counts[5:].min() > 64, counts
+    _free()
+
+
 def test_large_batch():
     # 262144 tokens x top-2: half a million slots through the single-block grouping, the
     # router and the combine at scale (int32 row indexing well away from its limit)
