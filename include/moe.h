@@ -36,8 +36,12 @@
  *  - Activations and weights share one dtype (MOE_F32 or MOE_BF16).  Logits, gate weights
  *    and every accumulation are fp32; the router accumulates fp32 partial sums of 256
  *    products each into fp64.  The FFN hidden state H is stored in the layer dtype (bf16
- *    rounding to nearest even); the per-row expert outputs (y_perm) are fp32 for every layer
- *    dtype, and the output y is rounded once, in the combine, to the layer dtype.
+ *    rounding to nearest even); the per-row expert outputs (y_perm) that moe_expert_ffn and
+ *    moe_combine exchange are fp32 for every layer dtype, and the output y is rounded once, in
+ *    the combine, to the layer dtype.  Inside the fused forward (workspace only), a bf16 layer
+ *    with a shared expert, MOE_GATE_SOFTMAX_TOPK and k <= N / 8 keeps its routed rows, already
+ *    scaled by their gate weights, in bf16 (the shared expert's rows stay fp32); each of those
+ *    roundings moves y by at most 2^-8 of that row's value (bf16 unit roundoff).
  *  - Ownership: the caller owns every buffer, including the workspace sized by
  *    moe_workspace_size().  The library allocates no device memory, keeps no pointer after a
  *    call returns and holds no state across calls beyond the thread-local error text.

@@ -27,15 +27,23 @@ __device__ __forceinline__ void row8(const float* __restrict__ yp, long long par
     }
 }
 
+// Eight columns of routed row r stored in bf16 (row r at element r * d of the buffer).
+__device__ __forceinline__ void row8_bf16(const float* __restrict__ yp, size_t off, float v[8]) {
+    const bf16x8 b = *(const bf16x8*)((const bf16*)yp + off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)b[i];
+}
+
 // One block per token, one thread per 8 columns (the block is as wide as d / 8 allows), so a
 // whole output row is one pass.  Slots are taken four at a time: their rows are loaded before
 // any of them is added, which keeps four rows' loads in flight, and the adds still run in slot
-// order.  A dropped slot (inv < 0) or a slot past k is neither loaded nor added.
+// order.  A dropped slot (inv < 0) or a slot past k is neither loaded nor added.  With
+// routed_bf16 (one K part) the routed rows are bf16 and the shared expert's rows fp32.
 __global__ __launch_bounds__(1024) void combine_bf16_kernel(const float* __restrict__ yp,
                                                             const int32_t* __restrict__ inv,
                                                             const float* __restrict__ w,
                                                             bf16* __restrict__ y, int T, int k, int d,
-                                                            int has_shared, int nparts) {
+                                                            int has_shared, int nparts, int routed_bf16) {
     const int t = blockIdx.x;
     const int32_t* iv = inv + (size_t)t * k;
     const float* wv = w ? w + (size_t)t * k : nullptr;
@@ -57,7 +65,9 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const float* __restr
             float v[4][8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (ok[q]) row8(yp, part_stride, nparts, (size_t)r[q] * d + c, v[q]);   // uniform per block
+                if (!ok[q]) continue;                                                   // uniform per block
+                if (routed_bf16) row8_bf16(yp, (size_t)r[q] * d + c, v[q]);
+                else row8(yp, part_stride, nparts, (size_t)r[q] * d + c, v[q]);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -100,14 +110,14 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
 }
 
 hipError_t launch_combine(const void* y_perm, const int32_t* inv, const float* w, void* y, int T,
-                          int k, int d, int has_shared, int dtype, int nparts, hipStream_t s) {
+                          int k, int d, int has_shared, int dtype, int nparts, int routed_bf16, hipStream_t s) {
     if (T == 0) return hipSuccess;
     if (dtype == 1) {
         // one thread per 8 columns, in whole waves, at most 1024
         int threads = ((d / 8 + 63) / 64) * 64;
         threads = threads < 64 ? 64 : (threads > 1024 ? 1024 : threads);
         hipLaunchKernelGGL(combine_bf16_kernel, dim3(T), dim3(threads), 0, s, (const float*)y_perm, inv, w,
-                           (bf16*)y, T, k, d, has_shared, nparts < 1 ? 1 : nparts);
+                           (bf16*)y, T, k, d, has_shared, nparts < 1 ? 1 : nparts, routed_bf16);
     }
     else
         hipLaunchKernelGGL(combine_f32_kernel, dim3(T), dim3(256), 0, s, (const float*)y_perm, inv, w,

@@ -41,6 +41,8 @@ struct FfnKArgs {
     long long part_stride;  // elements between the fp32 partial outputs of the K parts
     int small_rows;         // > 0: routed experts with 1 .. small_rows rows go to the weight-stream
                             // kernel, and the tiled kernels leave them out
+    int routed_bf16;        // out-projection, one K part: routed rows stored in bf16 (row r at
+                            // element r * Ncols of C viewed as bf16), the shared rows in fp32
     unsigned int* ctr;      // claiming GEMM: its schedule memory, 8 claim counters and from
                             // word FFN_CTR_BYTES / 4 on the tile table (ffn_tile_table)
 };
@@ -646,6 +648,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
     auto store = [&](const Acc& acc, auto nv) {
         const int m0 = cur.row_beg + cur.mt * BM, n0 = cur.nt * BNH;
         const float* scl = s_scale + (MODE == MODE_OUT ? (it & 1) * BM : 0);
+        const bool row_b16 = MODE == MODE_OUT && a.routed_bf16 && cur.seg < a.N;   // uniform
         // computed here, not hoisted above the K loop where they would hold registers
         int ln = lane;
         asm volatile("" : "+v"(ln));
@@ -672,7 +675,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_bf16_kernel(FfnKArgs a) {
                         else if (MODE == MODE_IN_RELU) v[e] = fmaxf(x, 0.f);
                         else v[e] = x * scale;
                     }
-                    if (MODE == MODE_OUT) {
+                    if (MODE == MODE_OUT && !row_b16) {
                         float4 o = {v[0], v[1], v[2], v[3]};
                         *(float4*)((float*)a.C + cur.kpart * a.part_stride + base + j * 32 + 8 * g) = o;
                     } else {
@@ -1268,6 +1271,23 @@ hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Routed rows of the out-projection in bf16: on bf16 layers with a shared expert, in one K part,
+// on the tiled path, when the caller reads that format.  The fused forward allows it for
+// fine-grained layers (k <= N / 8) whose gate weights are probabilities of a softmax over all N
+// experts.  The shared expert's row carries weight 1 and stays fp32; a routed row is already
+// scaled by its gate weight, and rounding it moves y by at most 2^-8 of that row's value (bf16's
+// unit roundoff), so the routed rows add at most 2^-8 * sum_j w_j |f_j|, sum_j w_j being the mass of
+// the k picks (about 0.2 for 8 of 256 experts).  Measured on one box: DeepSeek-V3 shape
+// 7.35-7.39 -> 7.17 ms per layer (combine 0.43 -> 0.25 ms, down projection 2.52 -> 2.44), shared +
+// top-7 of 256 6.99 -> 6.77-6.84, max|err|/RMS against the oracle unchanged (1.902e-2).  Where
+// the picks hold most of the mass (1 of 2 or 2 of 4 experts) the routed rows carry as much of y
+// as the shared one, and small layers of that kind measured 1.43e-2 -> 1.89e-2 with bf16 rows;
+// they, and layers with renormalised top-k weights, keep fp32 rows.
+int ffn_out_routed_bf16(const FfnLaunch& f) {
+    return f.routed_bf16_ok && f.dtype == 1 && f.has_shared && f.ksplit <= 1 && !skinny(f) &&
+           f.row_scale != nullptr;
+}
+
 hipError_t launch_ffn_out(const FfnLaunch& f, hipStream_t s) {
     if (f.T == 0) return hipSuccess;
     if (f.dtype == 1) {
@@ -1284,6 +1304,7 @@ hipError_t launch_ffn_out(const FfnLaunch& f, hipStream_t s) {
         a.ksplit = f.ksplit;
         a.part_stride = (long long)((long long)f.T * f.k + (f.has_shared ? f.T : 0)) * f.d;
         a.ctr = f.ctr;
+        a.routed_bf16 = ffn_out_routed_bf16(f);
         if (skinny(f)) return launch_skinny<MODE_OUT, SK_U_OUT, SK_CG_OUT>(a, s);
         // eight waves (2 x 4, two per SIMD) for the out-projection: measured on the same box,
         // Mixtral down projection 0.94 vs 1.01 ms with four, skewed 0.89 vs 0.93, DeepSeek-V3

@@ -274,7 +274,7 @@ moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int
     const moe_layer_desc& d = *desc;
     if (d.T == 0) return MOE_OK;
     if (!y_perm || !inv || !y) return fail(MOE_ERR_INVALID_ARG, "y_perm, inv and y are required");
-    hipError_t e = launch_combine(y_perm, inv, w, y, d.T, d.k, d.d, d.has_shared, d.dtype, 1, (hipStream_t)stream);
+    hipError_t e = launch_combine(y_perm, inv, w, y, d.T, d.k, d.d, d.has_shared, d.dtype, 1, 0, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 
@@ -318,13 +318,18 @@ moe_status forward_impl(const moe_layer_desc& d, const moe_weights& weights, con
     f.sched_bytes = sched_bytes(d, ksplit_of(d));
     if (q4) f.q4 = *q4;
     f.ksplit = q4 ? 1 : ksplit_of(d);
+    // the expert outputs are this call's own workspace: on fine-grained layers whose gate weights
+    // are probabilities of a softmax over all experts, routed rows may be stored in bf16
+    // (ffn_out_routed_bf16 has the rest of the rule and the reason)
+    f.routed_bf16_ok = (!q4 && d.gating == MOE_GATE_SOFTMAX_TOPK && 8LL * d.k <= d.N) ? 1 : 0;
+    const int routed_bf16 = ffn_out_routed_bf16(f);
     e = q4 ? launch_ffn_in_q4(f, s) : launch_ffn_in(f, s);
     if (e != hipSuccess) return hip_fail(e, "ffn in-projection launch");
     if ((st = record(ev(4), s)) != MOE_OK) return st;
     e = q4 ? launch_ffn_out_q4(f, s) : launch_ffn_out(f, s);
     if (e != hipSuccess) return hip_fail(e, "ffn out-projection launch");
     if ((st = record(ev(5), s)) != MOE_OK) return st;
-    e = launch_combine(yp, inv, nullptr, y, d.T, d.k, d.d, d.has_shared, d.dtype, f.ksplit, s);
+    e = launch_combine(yp, inv, nullptr, y, d.T, d.k, d.d, d.has_shared, d.dtype, f.ksplit, routed_bf16, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return record(ev(6), s);
 }

@@ -46,19 +46,23 @@ struct FfnLaunch {
     const void* sh_down;
     const float* row_scale;   // [T*k] or null
     void* h;                  // [T*k + T, d_ff] hidden state
-    void* y_perm;             // [ksplit][T*k + T, d] fp32 (ksplit partial sums)
+    void* y_perm;             // [ksplit][T*k + T, d] fp32 (ksplit partial sums); with routed
+                              // rows in bf16 (ffn_out_routed_bf16), row r < T*k is bf16 at element
+                              // r*d of the buffer viewed as bf16, the shared rows stay fp32
     int ksplit;               // K parts of the out-projection (1 = y_perm holds the result)
+    int routed_bf16_ok;       // the caller reads routed rows in bf16 where ffn_out_routed_bf16 says so
     unsigned int* ctr;        // the tiled GEMMs' schedule memory (claim counters, then a tile
     size_t sched_bytes;       // table), sched_bytes >= ffn_sched_bytes(); set up by the launches
     FfnQ4Weights q4;          // int4 weights (the q4 launchers only)
 };
 int ffn_out_ksplit(int T, int k, int N, int d, int d_ff, int has_shared, int dtype);
+int ffn_out_routed_bf16(const FfnLaunch& f);   // 1: launch_ffn_out stores routed rows in bf16
 #define FFN_CTR_BYTES 256
 size_t ffn_sched_bytes(int T, int k, int N, int d, int d_ff, int has_shared, int ksplit);
 hipError_t launch_ffn_in(const FfnLaunch& a, hipStream_t s);   // H = act(x W_in)
 hipError_t launch_ffn_out(const FfnLaunch& a, hipStream_t s);  // y_perm = scale * H W_out
 hipError_t launch_combine(const void* y_perm, const int32_t* inv, const float* w, void* y, int T,
-                          int k, int d, int has_shared, int dtype, int nparts, hipStream_t s);
+                          int k, int d, int has_shared, int dtype, int nparts, int routed_bf16, hipStream_t s);
 
 // Routing statistics: workspace of per-block partial sums, then the two-kernel launch.
 size_t stats_workspace_bytes(int T, int N);
