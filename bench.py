@@ -147,9 +147,13 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str
     write = per_kernel(write_dir, "WRITE_SIZE")
 
     def pick_in_projection(d):
-        # the gate/up (or W1) kernel: tiled or weight-streaming form, SwiGLU or ReLU mode
-        ks = [k for k in d if re.search(r"ffn_(bf16|skinny)_kernel<[01][,>]", k)]
-        return (statistics.mean(d[ks[0]]), ks[0]) if ks else (float("nan"), "none")
+        # the gate/up (or W1) stage, one launch of each of its kernels per layer call: the tiled
+        # GEMM, the weight-streaming kernel, or both (the tiled GEMM beside a weight stream for
+        # the small experts), SwiGLU or ReLU mode; the stage's bytes are their sum
+        ks = sorted(k for k in d if re.search(r"ffn_(bf16|skinny)_kernel<[01][,>]", k))
+        if not ks:
+            return float("nan"), "none"
+        return sum(statistics.mean(d[k]) for k in ks), " + ".join(ks)
 
     def largest(d, key):
         # the calibration copy is by far the largest copy dispatch of the run
@@ -162,7 +166,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str
     (ffn_f, kname), (ffn_w, _) = pick_in_projection(fetch), pick_in_projection(write)
     hbm = ffn_f * 1024.0 * f_scale + ffn_w * 1024.0 * w_scale
     lines = [
-        f"# HBM traffic of the grouped in-projection kernel ({kname}), {workload}",
+        f"# HBM traffic of the grouped in-projection stage ({kname}), {workload}",
         f"# command: {command}",
         "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by bytes/KiB it reads",
         f"# for a plain device copy of {copy_bytes} bytes in the same run.",
