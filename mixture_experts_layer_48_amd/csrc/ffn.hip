@@ -847,7 +847,12 @@ struct SkinnyTile {
 #ifndef SK_NT_MIN_CG
 #define SK_NT_MIN_CG 4
 #endif
-template <int MODE, int U, int CG, int RT>
+// SMALL: the launch beside a tiled GEMM, which runs only the routed experts of 1 .. small_rows
+// rows.  The check sits in that instantiation alone: compiled into the decode kernels as well (where
+// small_rows is 0 and it never returns), it slowed the Mixtral decode down projection from 0.139 to
+// 0.163 ms with an identical main loop (three interleaved pairs; a uniform form of the check and
+// 64-byte loop alignment did not recover it).
+template <int MODE, int U, int CG, int RT, bool SMALL>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
     using Tile = SkinnyTile<CG>;
     constexpr int NB = (MODE == MODE_IN_SWIGLU) ? 2 : 1;
@@ -876,8 +881,8 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
         if (NB == 2) B1 = a.S1;
     }
     if (row_end <= row_beg) return;                             // expert not touched
-    // with small_rows set, only the routed experts the tiled kernels leave out
-    if (a.small_rows > 0 && (seg >= a.N || row_end - row_beg > a.small_rows)) return;
+    // beside a tiled GEMM: only the routed experts it leaves out
+    if (SMALL && (seg >= a.N || row_end - row_beg > a.small_rows)) return;
     const int KS = a.K / 32 / nkp;                              // K steps of this wave
     const size_t step = (size_t)32 * a.Ncols;                   // elements between K steps
     B0 += (size_t)kp * KS * step;
@@ -1017,11 +1022,11 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(FfnKArgs a) {
     }
 }
 
-template <int MODE, int U, int CG, int RT = 1>
+template <int MODE, int U, int CG, int RT = 1, bool SMALL = false>
 static hipError_t launch_skinny(const FfnKArgs& a, hipStream_t s) {
     const int nkp = (MODE == MODE_OUT && a.ksplit > 1) ? a.ksplit : 1;
     const long long waves = (long long)(a.N + (a.has_shared ? 1 : 0)) * ((a.Ncols + 16 * CG - 1) / (16 * CG)) * nkp;
-    auto kern = ffn_skinny_kernel<MODE, U, CG, RT>;
+    auto kern = ffn_skinny_kernel<MODE, U, CG, RT, SMALL>;
     hipLaunchKernelGGL(kern, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
@@ -1250,7 +1255,7 @@ hipError_t launch_ffn_in(const FfnLaunch& f, hipStream_t s) {
                                : big_tiles(f) ? launch_bf16<MODE_IN_SWIGLU, 256, 128, 2, 2>(a, f.sched_bytes, s)
                                               : launch_bf16<MODE_IN_SWIGLU, 128, 128, 2, 2>(a, f.sched_bytes, s);
             if (e != hipSuccess || a.small_rows == 0) return e;
-            return launch_skinny<MODE_IN_SWIGLU, SK_U_IN, SK_CG_IN, FFN_SMALL_RT>(a, s);
+            return launch_skinny<MODE_IN_SWIGLU, SK_U_IN, SK_CG_IN, FFN_SMALL_RT, true>(a, s);
         }
         a.B0 = (const bf16*)f.w_up;
         a.S0 = (const bf16*)f.sh_up;
