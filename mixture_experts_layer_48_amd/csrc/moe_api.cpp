@@ -305,13 +305,28 @@ moe_status forward_impl(const moe_layer_desc& d, const moe_weights& weights, con
     void* yp = at(ws, L.yp);
 
     moe_status st;
+    hipError_t e;
     if ((st = record(ev(0), s)) != MOE_OK) return st;
-    st = stage_route(d, x, weights.w_router, weights.logit_bias, z, R.logits != nullptr, at(ws, L.h),
-                     (uint8_t*)at(ws, L.ranked), idx, w, s, ev(1));
-    if (st != MOE_OK) return st;
-    if ((st = record(ev(2), s)) != MOE_OK) return st;
-    hipError_t e = launch_permute(idx, d.T, d.k, d.N, counts, offsets, perm, inv, s);
-    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    if (!has_capacity(d) && !router_fused_supported(d.N, d.dtype) && route_finish_small_supported(d.T, d.N, d.k)) {
+        // a decode-sized batch: the router's logits (fp64 K-part sums), then their sum, top-k,
+        // gate weights and the grouping in one block (the stage events that follow mark empty
+        // stages)
+        void* rpart = at(ws, L.h);
+        e = launch_router_logits(x, weights.w_router, weights.logit_bias, z, rpart, d.T, d.d, d.N, d.dtype, s, false);
+        if (e != hipSuccess) return hip_fail(e, "router logits launch");
+        e = launch_route_finish_small(rpart, router_k_parts(d.T, d.d, d.N, d.dtype), weights.logit_bias, z, d.T, d.N,
+                                      d.k, d.gating, idx, w, counts, offsets, perm, inv, s);
+        if (e != hipSuccess) return hip_fail(e, "routing launch");
+        if ((st = record(ev(1), s)) != MOE_OK) return st;
+        if ((st = record(ev(2), s)) != MOE_OK) return st;
+    } else {
+        st = stage_route(d, x, weights.w_router, weights.logit_bias, z, R.logits != nullptr, at(ws, L.h),
+                         (uint8_t*)at(ws, L.ranked), idx, w, s, ev(1));
+        if (st != MOE_OK) return st;
+        if ((st = record(ev(2), s)) != MOE_OK) return st;
+        e = launch_permute(idx, d.T, d.k, d.N, counts, offsets, perm, inv, s);
+        if (e != hipSuccess) return hip_fail(e, "permute launch");
+    }
     if ((st = record(ev(3), s)) != MOE_OK) return st;
     FfnLaunch f = ffn_args(d, weights, x, perm, offsets, w, h, yp);
     f.ctr = (unsigned int*)at(ws, L.ctr);

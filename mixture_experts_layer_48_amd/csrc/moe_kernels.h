@@ -6,8 +6,17 @@
 
 // workspace of the router: fp64 partial logits [K parts, T, N] when K is split, else nothing
 size_t router_workspace_bytes(int T, int d, int N, int dtype);
+// sum_parts false: with K split (router_k_parts > 1) only the fp64 part sums are written (to ws),
+// for launch_route_finish_small to add up
 hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, float* z, void* ws,
-                                int T, int d, int N, int dtype, hipStream_t s);
+                                int T, int d, int N, int dtype, hipStream_t s, bool sum_parts = true);
+int router_k_parts(int T, int d, int N, int dtype);
+// a batch of at most 512 slots and 8192 logits: the K-part sum (when ks > 1), top-k, gate
+// weights and the grouping (counts, offsets, perm, inv) in one single-block launch
+bool route_finish_small_supported(int T, int N, int k);
+hipError_t launch_route_finish_small(const void* part, int ks, const float* bias, float* z, int T, int N, int k,
+                                     int gating, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                                     int32_t* perm, int32_t* inv, hipStream_t s);
 hipError_t launch_topk_gate(const float* z, int T, int N, int k, int gating, int32_t* idx, float* w,
                             hipStream_t s);
 // Router GEMM fused with top-k and softmax (bf16, N in {64, 128, 256}): writes the logits to z

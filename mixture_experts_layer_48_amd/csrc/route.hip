@@ -780,9 +780,90 @@ __global__ __launch_bounds__(256) void slot_gate_kernel(const float* __restrict_
     }
 }
 
+// ------------------------------------------------------------------ decode-sized batch: one finishing block
+// After the router's logits (or their fp64 K-part sums) for a batch of at most RF_MAX_S slots:
+// the K parts summed in part order with the bias and rounded once (as router_reduce_kernel),
+// top-k and the gate weights per token (topk_gate_wave, as topk_gate_kernel), and the grouping
+// (slot s = t k + j to row offsets[e] + the slots before s with expert e, so an expert's rows
+// are in ascending slot order, as permute_kernel) -- one launch where a 16-token decode batch had
+// three of 4-5 us each.
+#define RF_THREADS 512
+#define RF_WAVES (RF_THREADS / 64)
+#define RF_MAX_S 512                // slots (T * k)
+#define RF_MAX_Z 8192               // logits (T * N)
+
+__global__ __launch_bounds__(RF_THREADS) void route_finish_small_kernel(
+    const double* __restrict__ part, int ks, const float* __restrict__ bias, float* __restrict__ z, int T, int N,
+    int k, int gating, int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ float s_z[RF_MAX_Z];
+    __shared__ int32_t s_idx[RF_MAX_S];
+    __shared__ float s_w[RF_MAX_S];
+    __shared__ int s_cnt[MOE_MAX_EXPERTS];
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int TN = T * N, S = T * k;
+    for (int o = tid; o < TN; o += RF_THREADS) {
+        float zf;
+        if (ks > 1) {
+            double acc = 0.0;
+            for (int p = 0; p < ks; ++p) acc += part[(size_t)p * TN + o];
+            if (bias) acc += (double)bias[o % N];
+            zf = (float)acc;
+            z[o] = zf;
+        } else {
+            zf = z[o];                                     // written by the router itself
+        }
+        s_z[o] = zf;
+    }
+    __syncthreads();
+    for (int t = wave; t < T; t += RF_WAVES) {             // uniform per wave
+        float zl[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = lane + 64 * q;
+            zl[q] = e < N ? s_z[t * N + e] : 0.f;
+        }
+        topk_gate_wave(zl, lane, N, k, gating, s_idx + t * k, s_w + t * k);
+    }
+    __syncthreads();
+    for (int e = tid; e < N; e += RF_THREADS) {
+        int c = 0;
+        for (int i = 0; i < S; ++i) c += s_idx[i] == e ? 1 : 0;
+        s_cnt[e] = c;
+        counts[e] = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int e = 0; e < N; ++e) {
+            s_off[e] = run;
+            offsets[e] = run;
+            run += s_cnt[e];
+        }
+        s_off[N] = run;
+        offsets[N] = run;
+    }
+    __syncthreads();
+    for (int sl = tid; sl < S; sl += RF_THREADS) {
+        const int e = s_idx[sl];
+        int before = 0;
+        for (int i = 0; i < sl; ++i) before += s_idx[i] == e ? 1 : 0;
+        const int row = s_off[e] + before;
+        idx[sl] = e;
+        w[sl] = s_w[sl];
+        perm[row] = sl;
+        inv[sl] = row;
+    }
+}
+
 // ------------------------------------------------------------------ launchers
+int router_k_parts(int T, int d, int N, int dtype) {
+    return (dtype == 1 && T > 0) ? router_split(T, d, N).ks : 1;
+}
+
 hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, float* z, void* ws,
-                                int T, int d, int N, int dtype, hipStream_t s) {
+                                int T, int d, int N, int dtype, hipStream_t s, bool sum_parts) {
     if (T == 0) return hipSuccess;
     if (dtype == 1) {
         const RouterSplit sp = router_split(T, d, N);
@@ -802,7 +883,7 @@ hipError_t launch_router_logits(const void* x, const void* wr, const float* bias
             case 4: launch(std::integral_constant<int, 4>{}, n_full, 1); break;
             default: break;
         }
-        if (sp.ks > 1) {
+        if (sp.ks > 1 && sum_parts) {
             const long long n = (long long)T * N;
             hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                                (const double*)ws, bias, z, T, N, sp.ks);
@@ -816,6 +897,20 @@ hipError_t launch_router_logits(const void* x, const void* wr, const float* bias
 }
 
 bool router_fused_supported(int N, int dtype) { return dtype == 1 && (N == 64 || N == 128 || N == 256); }
+
+bool route_finish_small_supported(int T, int N, int k) {
+    return T >= 1 && k >= 1 && k <= N && N <= MOE_MAX_EXPERTS && (long long)T * k <= RF_MAX_S &&
+           (long long)T * N <= RF_MAX_Z;
+}
+
+hipError_t launch_route_finish_small(const void* part, int ks, const float* bias, float* z, int T, int N, int k,
+                                     int gating, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                                     int32_t* perm, int32_t* inv, hipStream_t s) {
+    if (!route_finish_small_supported(T, N, k) || (ks > 1 && !part)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_finish_small_kernel, dim3(1), dim3(RF_THREADS), 0, s, (const double*)part, ks, bias, z,
+                       T, N, k, gating, idx, w, counts, offsets, perm, inv);
+    return hipGetLastError();
+}
 
 hipError_t launch_router_topk(const void* x, const void* wr, const float* bias, float* z, int T, int d, int N,
                               int k, int gating, int32_t* idx, float* w, hipStream_t s) {
