@@ -115,6 +115,9 @@ SMALL = {
                                       ffn=W.FFN_SWIGLU, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=42),
     "fine_shared_t320": W.LayerConfig("fine_shared_t320", T=2048, d=256, N=64, k=8, d_ff=320, dtype="bf16",
                                       ffn=W.FFN_SWIGLU, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=43),
+    # 512 slots (128 tokens x top-4 of 32 experts, a logit bias): the routing finished in one block
+    "finish_limits": W.LayerConfig("finish_limits", T=128, d=256, N=32, k=4, d_ff=192, dtype="bf16",
+                                   ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, zipf_bias=True, seed=44),
     # at most 16 routed rows per expert on average: the weight-streaming decode GEMMs, here with a
     # shared expert longer than one 16-row tile, heavy experts, and capacity drops
     "skinny_relu_shared": W.LayerConfig("skinny_relu_shared", T=24, d=128, N=16, k=2, d_ff=192, dtype="bf16",

@@ -43,6 +43,10 @@ EXACT = {
                          seed=38), 32, True),
     "sel_decode": (LC("sel_decode", T=16, d=256, N=8, k=2, d_ff=256, dtype="bf16", ffn=SW, gating=TS, seed=39),
                    8, False),
+    # a batch at the single-block routing finish's limit of 512 slots (64 tokens x top-8), over 100
+    # experts (more than one wave's 64 lanes, an expert count the fused router does not take)
+    "sel_finish_limits": (LC("sel_finish_limits", T=64, d=256, N=100, k=8, d_ff=64, dtype="bf16", ffn=SW,
+                             gating=ST, seed=40), 16, True),
 }
 
 
