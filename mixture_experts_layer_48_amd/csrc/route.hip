@@ -160,8 +160,16 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const double* __rest
     const long long o = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const long long TN = (long long)T * N;
     if (o >= TN) return;
+    // parts loaded eight at a time, then added in part order
     double acc = 0.0;
-    for (int p = 0; p < ks; ++p) acc += part[p * TN + o];
+    for (int p0 = 0; p0 < ks; p0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = p0 + i < ks ? part[(p0 + i) * TN + o] : 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (p0 + i < ks) acc += v[i];
+    }
     if (bias) acc += (double)bias[o % N];
     z[o] = (float)acc;
 }
@@ -806,8 +814,16 @@ __global__ __launch_bounds__(RF_THREADS) void route_finish_small_kernel(
     for (int o = tid; o < TN; o += RF_THREADS) {
         float zf;
         if (ks > 1) {
+            // parts loaded eight at a time, then added in part order
             double acc = 0.0;
-            for (int p = 0; p < ks; ++p) acc += part[(size_t)p * TN + o];
+            for (int p0 = 0; p0 < ks; p0 += 8) {
+                double v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = p0 + i < ks ? part[(size_t)(p0 + i) * TN + o] : 0.0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (p0 + i < ks) acc += v[i];
+            }
             if (bias) acc += (double)bias[o % N];
             zf = (float)acc;
             z[o] = zf;
