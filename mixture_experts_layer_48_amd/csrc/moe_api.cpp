@@ -19,6 +19,10 @@
 // device address comes from hipGetSymbolAddress, once per device (noalloc_scratch below).
 static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
+// slots (T * k) from which the fused forward groups them over many blocks: measured on the
+// DeepSeek-V3 shape (65536 slots) and the skewed layer (32768); the single block stays below
+#define PERMUTE_MULTI_MIN_SLOTS 16384
+
 namespace {
 
 thread_local std::string g_err;
@@ -115,8 +119,10 @@ Layout layout_of(const moe_layer_desc& d) {
     L.perm = o; o += align256(T * k * 4);
     L.inv = o; o += align256(T * k * 4);
     // the router's partial logits are dead before the hidden state is written: they share space
-    L.h = o; o += std::max(align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d)),
-                           align256(router_workspace_bytes(d.T, d.d, d.N, d.dtype)));
+    // (before H is written it holds the router's K-part sums, then the grouping's block counts)
+    L.h = o; o += std::max({align256((size_t)rows_total(d) * d.d_ff * elem_bytes(d)),
+                            align256(router_workspace_bytes(d.T, d.d, d.N, d.dtype)),
+                            align256(permute_multi_workspace_bytes(d.T, d.k, d.N))});
     // fp32 expert rows, one copy per K part of the out-projection
     L.yp = o; o += align256((size_t)rows_total(d) * d.d * 4 * ksplit_of(d));
     // the grouped GEMMs' schedule: tile-claim counters and a tile table
@@ -324,7 +330,12 @@ moe_status forward_impl(const moe_layer_desc& d, const moe_weights& weights, con
                          (uint8_t*)at(ws, L.ranked), idx, w, s, ev(1));
         if (st != MOE_OK) return st;
         if ((st = record(ev(2), s)) != MOE_OK) return st;
-        e = launch_permute(idx, d.T, d.k, d.N, counts, offsets, perm, inv, s);
+        // large slot counts: the grouping over many blocks, its per-block counts in the hidden
+        // state's region (unused until the in-projection)
+        if ((long long)d.T * d.k >= PERMUTE_MULTI_MIN_SLOTS)
+            e = launch_permute_multi(idx, d.T, d.k, d.N, counts, offsets, perm, inv, (int32_t*)at(ws, L.h), s);
+        else
+            e = launch_permute(idx, d.T, d.k, d.N, counts, offsets, perm, inv, s);
         if (e != hipSuccess) return hip_fail(e, "permute launch");
     }
     if ((st = record(ev(3), s)) != MOE_OK) return st;

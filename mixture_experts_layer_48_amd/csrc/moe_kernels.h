@@ -31,6 +31,11 @@ hipError_t launch_capacity(const float* z, uint8_t* ranked, int T, int N, int k,
                            int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int N, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, hipStream_t s);
+// the same grouping over many blocks (for large T * k): per-block counts in ws, [ceil(T*k/1024), N]
+// int32 (permute_multi_workspace_bytes), then a scan and the placement; bit-identical results
+size_t permute_multi_workspace_bytes(int T, int k, int N);
+hipError_t launch_permute_multi(const int32_t* idx, int T, int k, int N, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, int32_t* ws, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* perm, const int32_t* offsets, int T,
                               int k, int N, int row_bytes, void* x_perm, hipStream_t s);
 

@@ -166,6 +166,122 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(
     }
 }
 
+// The same grouping over many blocks, for large slot counts (the fused forward, which has a
+// workspace for the per-block counts): one block of 1024 threads does 1024 slots' worth of it,
+// where the single block above walks every slot in 64-slot groups (65536 slots of the
+// DeepSeek-V3 shape: 66 us on one CU).
+//   1. permute_count_kernel: block b counts its slots per expert;
+//   2. permute_scan_kernel (one block): counts, the exclusive scan over experts (offsets), and in
+//      place of each block's count its first row for that expert (offsets[e] + the counts of e in
+//      earlier blocks);
+//   3. permute_place_kernel: a slot's row is its block's first row for its expert, plus the
+//      slots with that expert in earlier waves of the block, plus the lower lanes of its own wave
+//      with that expert (ballot matching): rows of an expert are in ascending slot order, so the
+//      result is the single-block kernel's, bit for bit.
+#define PMB_SLOTS 1024
+#define PMB_WAVES (PMB_SLOTS / 64)
+
+__global__ __launch_bounds__(PMB_SLOTS) void permute_count_kernel(const int32_t* __restrict__ idx, int S, int N,
+                                                                  int32_t* __restrict__ cnt) {
+    __shared__ int h[MOE_MAX_EXPERTS];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < N; e += PMB_SLOTS) h[e] = 0;
+    __syncthreads();
+    const int s = blockIdx.x * PMB_SLOTS + tid;
+    const int e = s < S ? idx[s] : -1;
+    if (e >= 0 && e < N) atomicAdd(&h[e], 1);              // integer counts: order-independent
+    __syncthreads();
+    for (int x = tid; x < N; x += PMB_SLOTS) cnt[(size_t)blockIdx.x * N + x] = h[x];
+}
+
+__global__ __launch_bounds__(MOE_MAX_EXPERTS) void permute_scan_kernel(int32_t* __restrict__ cnt, int B, int N,
+                                                                       int32_t* __restrict__ counts,
+                                                                       int32_t* __restrict__ offsets) {
+    __shared__ int s_tot[MOE_MAX_EXPERTS];
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    const int tid = threadIdx.x;                           // one thread per expert (N <= 256)
+    auto sum_blocks = [&](int e) {                         // block counts loaded eight at a time
+        int tot = 0;
+        for (int b0 = 0; b0 < B; b0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = b0 + i < B ? cnt[(size_t)(b0 + i) * N + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) tot += v[i];
+        }
+        return tot;
+    };
+    if (tid < N) s_tot[tid] = sum_blocks(tid);
+    __syncthreads();
+    if (tid < 64) {  // one wave: exclusive scan over experts, four per lane
+        int tot[4], run = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid * 4 + q;
+            tot[q] = e < N ? s_tot[e] : 0;
+            run += tot[q];
+        }
+        int incl = run;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (tid >= o) incl += v;
+        }
+        int base = incl - run;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid * 4 + q;
+            if (e < N) {
+                s_off[e] = base;
+                counts[e] = tot[q];
+                offsets[e] = base;
+            }
+            base += tot[q];
+        }
+        if (tid == 63) offsets[N] = incl;
+    }
+    __syncthreads();
+    if (tid < N) {
+        int run = s_off[tid];
+        for (int b0 = 0; b0 < B; b0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = b0 + i < B ? cnt[(size_t)(b0 + i) * N + tid] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (b0 + i < B) {
+                    cnt[(size_t)(b0 + i) * N + tid] = run;
+                    run += v[i];
+                }
+        }
+    }
+}
+
+__global__ __launch_bounds__(PMB_SLOTS) void permute_place_kernel(const int32_t* __restrict__ idx, int S, int N,
+                                                                  const int32_t* __restrict__ base,
+                                                                  int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ int cw[PMB_WAVES][MOE_MAX_EXPERTS];        // slots per expert in each wave
+    const int tid = threadIdx.x, wave = tid >> 6;
+    for (int i = tid; i < PMB_WAVES * N; i += PMB_SLOTS) cw[i / N][i % N] = 0;
+    __syncthreads();
+    const int s = blockIdx.x * PMB_SLOTS + tid;
+    const bool valid = s < S;
+    const int ev = valid ? idx[s] : -1;
+    const int e = (ev >= 0 && ev < N) ? ev : -1;
+    const uint64_t eq = match_lanes<9>((uint32_t)(e + 1));  // every lane takes part
+    const int rin = __popcll(eq & lanemask_lt());
+    if (e >= 0 && rin == 0) cw[wave][e] = __popcll(eq);
+    __syncthreads();
+    if (e >= 0) {
+        int r = base[(size_t)blockIdx.x * N + e] + rin;
+        for (int w = 0; w < wave; ++w) r += cw[w][e];
+        perm[r] = s;
+        inv[s] = r;
+    } else if (valid) {
+        inv[s] = -1;
+    }
+}
+
 // Optional materialised gather: x_perm[r] = x[perm[r] / k] for r < offsets[N].
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ x,
                                                           const int32_t* __restrict__ perm,
@@ -189,6 +305,23 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int N, int32_t* coun
     const int S = T * k;
     permute_kernel<false, NoMapArg><<<1, PM_THREADS, 0, s>>>(idx, S, N, counts, offsets, perm, inv, NoMapArg{},
                                                              nullptr, nullptr);
+    return hipGetLastError();
+}
+
+size_t permute_multi_workspace_bytes(int T, int k, int N) {
+    const long long S = (long long)T * k;
+    return (size_t)((S + PMB_SLOTS - 1) / PMB_SLOTS) * N * sizeof(int32_t);
+}
+
+hipError_t launch_permute_multi(const int32_t* idx, int T, int k, int N, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, int32_t* ws, hipStream_t s) {
+    const int S = T * k;
+    if (S == 0) return hipSuccess;
+    if (N > MOE_MAX_EXPERTS || !ws) return hipErrorInvalidValue;
+    const int B = (S + PMB_SLOTS - 1) / PMB_SLOTS;
+    permute_count_kernel<<<B, PMB_SLOTS, 0, s>>>(idx, S, N, ws);
+    permute_scan_kernel<<<1, MOE_MAX_EXPERTS, 0, s>>>(ws, B, N, counts, offsets);
+    permute_place_kernel<<<B, PMB_SLOTS, 0, s>>>(idx, S, N, ws, perm, inv);
     return hipGetLastError();
 }
 

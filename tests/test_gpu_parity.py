@@ -115,6 +115,11 @@ SMALL = {
                                       ffn=W.FFN_SWIGLU, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=42),
     "fine_shared_t320": W.LayerConfig("fine_shared_t320", T=2048, d=256, N=64, k=8, d_ff=320, dtype="bf16",
                                       ffn=W.FFN_SWIGLU, gating=W.GATE_SOFTMAX_TOPK, has_shared=True, seed=43),
+    # 16384 slots with capacity drops: the grouping over many blocks (drops left out of every
+    # expert's rows)
+    "capacity_drops_many": W.LayerConfig("capacity_drops_many", T=8192, d=64, N=64, k=2, d_ff=64, dtype="bf16",
+                                         ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, capacity_factor=0.5,
+                                         zipf_bias=True, seed=45),
     # 512 slots (128 tokens x top-4 of 32 experts, a logit bias): the routing finished in one block
     "finish_limits": W.LayerConfig("finish_limits", T=128, d=256, N=32, k=4, d_ff=192, dtype="bf16",
                                    ffn=W.FFN_SWIGLU, gating=W.GATE_TOPK_SOFTMAX, zipf_bias=True, seed=44),
