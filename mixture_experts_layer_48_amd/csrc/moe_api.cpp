@@ -19,9 +19,10 @@
 // device address comes from hipGetSymbolAddress, once per device (noalloc_scratch below).
 static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
-// slots (T * k) from which the fused forward groups them over many blocks: measured on the
-// DeepSeek-V3 shape (65536 slots) and the skewed layer (32768); the single block stays below
-#define PERMUTE_MULTI_MIN_SLOTS 16384
+// slots (T * k) from which the fused forward groups them over many blocks, measured against the
+// single block: 65536 slots (DeepSeek-V3 shape) 0.077 -> 0.025 ms, 32768 (skewed layer) 0.036 ->
+// 0.016 ms, 8192 (Mixtral prefill) 14.0 -> 12.7 us; at 4096 (top-1 of 16) 10-12 -> 12.3 us
+#define PERMUTE_MULTI_MIN_SLOTS 8192
 
 namespace {
 
