@@ -159,6 +159,13 @@ moe_status stage_route(const moe_layer_desc& d, const void* x, const void* wr, c
         e = launch_router_topk(x, wr, bias, (want_z || cap) ? z : nullptr, d.T, d.d, d.N, d.k, d.gating,
                                cap ? nullptr : idx, w, s);
         if (e != hipSuccess) return hip_fail(e, "router launch");
+    } else if (!has_capacity(d) && router_k_parts(d.T, d.d, d.N, d.dtype) > 1) {
+        // the K-part sum and top-k in one launch
+        e = launch_router_logits(x, wr, bias, z, rpart, d.T, d.d, d.N, d.dtype, s, false);
+        if (e != hipSuccess) return hip_fail(e, "router logits launch");
+        e = launch_reduce_topk(rpart, router_k_parts(d.T, d.d, d.N, d.dtype), bias, z, d.T, d.N, d.k, d.gating, idx, w,
+                               s);
+        if (e != hipSuccess) return hip_fail(e, "top-k launch");
     } else {
         e = launch_router_logits(x, wr, bias, z, rpart, d.T, d.d, d.N, d.dtype, s);
         if (e != hipSuccess) return hip_fail(e, "router logits launch");

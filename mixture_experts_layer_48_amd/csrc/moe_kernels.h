@@ -11,6 +11,10 @@ size_t router_workspace_bytes(int T, int d, int N, int dtype);
 hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, float* z, void* ws,
                                 int T, int d, int N, int dtype, hipStream_t s, bool sum_parts = true);
 int router_k_parts(int T, int d, int N, int dtype);
+// the fp64 K-part sums of launch_router_logits (sum_parts false, ks > 1) summed into z and ranked:
+// idx / w [T, k], one launch
+hipError_t launch_reduce_topk(const void* part, int ks, const float* bias, float* z, int T, int N, int k,
+                             int gating, int32_t* idx, float* w, hipStream_t s);
 // a batch of at most 512 slots and 8192 logits: the K-part sum (when ks > 1), top-k, gate
 // weights and the grouping (counts, offsets, perm, inv) in one single-block launch
 bool route_finish_small_supported(int T, int N, int k);

@@ -788,6 +788,42 @@ __global__ __launch_bounds__(256) void slot_gate_kernel(const float* __restrict_
     }
 }
 
+// The K-part sum and top-k in one launch (layers without capacity whose expert count the fused
+// router does not take): one wave per token sums its N logits' fp64 parts in part order, adds
+// the bias and rounds once (as router_reduce_kernel), writes the logits, and ranks them with
+// topk_gate_wave (as topk_gate_kernel).
+__global__ __launch_bounds__(256) void reduce_topk_kernel(const double* __restrict__ part, int ks,
+                                                          const float* __restrict__ bias, float* __restrict__ z,
+                                                          int T, int N, int k, int gating, int32_t* __restrict__ idx,
+                                                          float* __restrict__ w) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;  // whole wave leaves together; no block barrier below
+    const long long TN = (long long)T * N;
+    float zl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        zl[q] = 0.f;
+        if (e < N) {
+            const long long o = (long long)t * N + e;
+            double acc = 0.0;                            // parts loaded eight at a time, added in order
+            for (int p0 = 0; p0 < ks; p0 += 8) {
+                double v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = p0 + i < ks ? part[(p0 + i) * TN + o] : 0.0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (p0 + i < ks) acc += v[i];
+            }
+            if (bias) acc += (double)bias[e];
+            zl[q] = (float)acc;
+            z[o] = zl[q];
+        }
+    }
+    topk_gate_wave(zl, lane, N, k, gating, idx + (size_t)t * k, w + (size_t)t * k);
+}
+
 // ------------------------------------------------------------------ decode-sized batch: one finishing block
 // After the router's logits (or their fp64 K-part sums) for a batch of at most RF_MAX_S slots:
 // the K parts summed in part order with the bias and rounded once (as router_reduce_kernel),
@@ -941,6 +977,15 @@ hipError_t launch_router_topk(const void* x, const void* wr, const float* bias, 
     else if (N == 128) go(router_topk_kernel<128>);
     else if (N == 256) go(router_topk_kernel<256>);
     else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_topk(const void* part, int ks, const float* bias, float* z, int T, int N, int k,
+                             int gating, int32_t* idx, float* w, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (!part || ks < 1 || N > MOE_MAX_EXPERTS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(reduce_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, (const double*)part, ks, bias, z, T,
+                       N, k, gating, idx, w);
     return hipGetLastError();
 }
 

@@ -43,6 +43,9 @@ EXACT = {
                          seed=38), 32, True),
     "sel_decode": (LC("sel_decode", T=16, d=256, N=8, k=2, d_ff=256, dtype="bf16", ffn=SW, gating=TS, seed=39),
                    8, False),
+    # K split in four parts (d = 1024) and summed in the same launch as top-k (1400 slots)
+    "sel_reduce_topk": (LC("sel_reduce_topk", T=700, d=1024, N=16, k=2, d_ff=64, dtype="bf16", ffn=SW, gating=TS,
+                           seed=41), 8, True),
     # a batch at the single-block routing finish's limit of 512 slots (64 tokens x top-8), over 100
     # experts (more than one wave's 64 lanes, an expert count the fused router does not take)
     "sel_finish_limits": (LC("sel_finish_limits", T=64, d=256, N=100, k=8, d_ff=64, dtype="bf16", ffn=SW,
