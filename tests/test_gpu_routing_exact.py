@@ -43,6 +43,9 @@ EXACT = {
                          seed=38), 32, True),
     "sel_decode": (LC("sel_decode", T=16, d=256, N=8, k=2, d_ff=256, dtype="bf16", ffn=SW, gating=TS, seed=39),
                    8, False),
+    # 16384 slots with capacity drops: the grouping over many blocks, bit for bit
+    "sel_capacity_many": (LC("sel_capacity_many", T=8192, d=64, N=64, k=2, d_ff=64, dtype="bf16", ffn=SW,
+                             gating=TS, capacity_factor=0.5, seed=42), 8, True),
     # K split in four parts (d = 1024) and summed in the same launch as top-k (1400 slots)
     "sel_reduce_topk": (LC("sel_reduce_topk", T=700, d=1024, N=16, k=2, d_ff=64, dtype="bf16", ffn=SW, gating=TS,
                            seed=41), 8, True),
